@@ -1,0 +1,212 @@
+"""Benchmark of the sharded-matmul hot path on one MI355X.
+
+One step = one pass of the whole path over the case-3 down-projection
+workload (mesh {X:4, Y:2}, A[I_X, J_Y] . B[J_Y, K] with I = K = 8192,
+J = 28672; the sharding sandbox default of learntpu.dev ch05):
+  1. sm_plan (host),
+  2. sm_local_gemm: the 8 logical ranks' local products
+     [2048,14336] . [14336,8192] -> 8 fp32 partials, one launch,
+  3. sm_reduce_partials(REDUCESCATTER): 4 groups x 2 partials -> row blocks
+     [1024,8192] of the finished C, one launch.
+Inputs are resident in HBM before the timed region. One JSON line on stdout.
+
+The HIP events that time each kernel are recorded on the stream the kernels
+are launched on. `--copy-calibration` runs a plain device copy of a known
+size (for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE counters).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA
+PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
+METRIC = "shard GEMM TFLOP/s (% bf16 MFMA peak) + partial-reduce GB/s (% HBM peak)"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def setup(workload: str):
+    import torch
+
+    import local_shard_gemm_amd as sm
+    import workloads as wl
+
+    w = wl.get(workload)
+    names = [o.name for o in w.operands]
+    A = wl.make_operand(w.operand(names[0]))
+    B = wl.make_operand(w.operand(names[1]))
+    I, J = A.shape
+    K = B.shape[1]
+    dev = torch.device("cuda:0")
+    p = sm.sm_plan(dict(w.mesh), w.operand(names[0]).spec, w.operand(names[1]).spec, I, J, K)
+    Ad, Bd = A.to(dev), B.to(dev)
+    m, n = p.c_local[0], p.c_local[1]
+    P = torch.empty(p.n_units, m, n, dtype=torch.float32, device=dev)
+    if p.kase == sm.SM_CASE3 and m % p.n_partials == 0:
+        mode = sm.SM_REDUCESCATTER
+        out = torch.empty(I, K, dtype=torch.float32, device=dev)
+    else:
+        mode = sm.SM_ALLREDUCE
+        out = torch.empty(p.n_groups, m, n, dtype=torch.float32, device=dev)
+    return dict(w=w, A=A, B=B, p=p, Ad=Ad, Bd=Bd, P=P, out=out, mode=mode, I=I, J=J, K=K)
+
+
+def cpu_baseline(ctx, rows: int):
+    """The oracle (fp64 naive loops) on a bounded sample: `rows` output rows
+    of unit 0's local product, timed on the host cores."""
+    import numpy as np
+
+    from oracle import planner, reference as ref
+    from oracle.build import load_library
+
+    w = ctx["w"]
+    names = [o.name for o in w.operands]
+    q = planner.plan(dict(w.mesh), w.operand(names[0]).spec, w.operand(names[1]).spec, ctx["I"], ctx["J"], ctx["K"])
+    m, n = q.c_local
+    k = q.a_local[1]
+    rows = min(rows, m)
+    sel = np.arange(rows)
+    t0 = time.perf_counter()
+    ref.unit_partial(q, ctx["A"], ctx["B"], 0, rows=sel)
+    dt = time.perf_counter() - t0
+    flops = 2.0 * rows * n * k
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(load_library().orc_num_threads()),
+            "kind": "oracle",
+            "sample": f"{rows} output rows of unit 0's local product [{m},{k}]x[{k},{n}] "
+                      f"({flops / 1e9:.1f} GFLOP, fp64 naive loops, {dt:.1f} s)"}
+
+
+def copy_calibration(mib: int, reps: int) -> None:
+    import torch
+
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_each_way": n * 4, "reps": reps}), flush=True)
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="downproj")
+    ap.add_argument("--cpu-rows", type=int, default=768, help="oracle sample size (rows of unit 0)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: every logical rank's shards are resident on a single "
+              "MI355X; runs on more than one GPU are not part of this build.", file=sys.stderr)
+        return 2
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration, 5)
+        return 0
+
+    import torch
+
+    import local_shard_gemm_amd as sm
+
+    log(f"bench: setting up workload {args.workload}")
+    ctx = setup(args.workload)
+    p, P, out, mode = ctx["p"], ctx["P"], ctx["out"], ctx["mode"]
+    a, b, c, o = sm.buf(ctx["Ad"]), sm.buf(ctx["Bd"]), sm.buf(P), sm.buf(out)
+    stream = torch.cuda.current_stream()
+
+    def step(evs=None):
+        if evs:
+            evs[0].record(stream)
+        sm.sm_local_gemm(p, a, b, c, sm.SM_EPI_STORE, 0, p.n_units, stream)
+        if evs:
+            evs[1].record(stream)
+        if p.kase == sm.SM_CASE3:
+            sm.sm_reduce_partials(p, c, o, mode, 0, p.n_groups, stream)
+        if evs:
+            evs[2].record(stream)
+
+    log(f"bench: warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    log(f"bench: timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step(evs[k])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / args.steps
+    gemm_ms = sorted(e[0].elapsed_time(e[1]) for e in evs)
+    red_ms = sorted(e[1].elapsed_time(e[2]) for e in evs)
+    gemm_avg = sum(gemm_ms) / len(gemm_ms)
+    red_avg = sum(red_ms) / len(red_ms)
+
+    m, n = p.c_local[0], p.c_local[1]
+    k = p.a_local[1]
+    gemm_flops = 2.0 * m * n * k * p.n_units
+    N = p.n_partials
+    # reduce: each group reads N fp32 partials and writes one fp32 block
+    red_bytes = (N + 1) * m * n * 4.0 * p.n_groups if p.kase == sm.SM_CASE3 else 0.0
+    gemm_tflops = gemm_flops / (gemm_avg * 1e-3) / 1e12
+    red_gbps = red_bytes / (red_avg * 1e-3) / 1e9 if red_bytes else 0.0
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log(f"bench: oracle CPU baseline on {args.cpu_rows} rows")
+        cpu = cpu_baseline(ctx, args.cpu_rows)
+
+    line = {
+        "metric": METRIC,
+        "value": round(gemm_flops / (ms_step * 1e-3) / 1e12, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": ctx["w"].name,
+            "mesh": "{X:4,Y:2}" if args.workload == "downproj" else str(dict(ctx["w"].mesh)),
+            "global": f"A[{ctx['I']},{ctx['J']}] . B[{ctx['J']},{ctx['K']}]",
+            "units": int(p.n_units),
+            "local_gemm": f"[{m},{k}]x[{k},{n}] bf16 -> fp32",
+            "reduce": ("reduce-scatter" if mode == sm.SM_REDUCESCATTER else "all-reduce")
+                      + f" {p.n_groups} groups x {N} fp32 partials [{m},{n}]",
+        },
+        "gemm": {"avg_ms": round(gemm_avg, 4), "min_ms": round(gemm_ms[0], 4),
+                 "tflops": round(gemm_tflops, 1), "frac_of_peak": round(gemm_tflops / PEAK_BF16_TFLOPS, 4)},
+        "reduce": {"avg_ms": round(red_avg, 4), "min_ms": round(red_ms[0], 4), "bytes": red_bytes,
+                   "gbps": round(red_gbps, 1), "frac_of_peak": round(red_gbps / PEAK_HBM_GBPS, 4)},
+        "roofline": {"bound": "mfma", "achieved": round(gemm_tflops, 1), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(gemm_tflops / PEAK_BF16_TFLOPS, 4), "traffic": None},
+        "roofline_reduce": {"bound": "hbm", "achieved": round(red_gbps, 1), "peak": PEAK_HBM_GBPS,
+                            "unit": "GB/s", "frac": round(red_gbps / PEAK_HBM_GBPS, 4), "traffic": None},
+        "cpu_baseline": cpu,
+        "context": "learntpu.dev sandbox, modelled (not measured) on Ironwood: 481 GFLOP local matmul "
+                   "in 209 us per rank",
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

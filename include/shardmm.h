@@ -1,0 +1,228 @@
+/*
+ * shardmm.h -- C ABI of libshardmm, the sharded-matmul hot path on one
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The operation is A[I,J] . B[J,K] -> C[I,K] with J contracted, laid out on
+ * a mesh of named axes ("logical ranks"). Every logical rank's shards stay
+ * resident on the one GPU; the library computes each rank's local product
+ * and finishes what the collectives of a multi-device run would finish:
+ * the sum of unreduced partials (all-reduce or reduce-scatter semantics)
+ * and the assembly of finished blocks (all-gather).
+ *
+ * Sources: lingze.zone "Cheetsheet for the four cases of sharded matmul"
+ * (sections Notation, Case 1-4, Summary); learntpu.dev ch05 "Sharded
+ * matmuls and collectives on a torus" (Notation table, the four cases, the
+ * sharding sandbox, the table of the four collectives); semiaifoundry.com
+ * "Sharded matrix multiplication and result ownership" (The mechanism,
+ * Engineering example, Interfaces); mbrenndoerfer.com "Row Parallelism"
+ * (Y = X A = sum_i X_i A_i).
+ *
+ * Conventions for every call
+ *  - Return value: an sm_status (0 = SM_OK). Nothing is thrown across the
+ *    ABI. sm_last_error() gives a thread-local text for the last failure.
+ *  - All argument checks run on the host before anything is enqueued, so a
+ *    non-OK status other than SM_ERR_HIP leaves every output untouched.
+ *  - Memory: every device buffer is allocated and freed by the caller. The
+ *    library allocates no device memory, keeps no device state, starts no
+ *    threads. Plans are caller-owned plain structs that need no freeing.
+ *  - Streams: device calls enqueue on the given stream (a hipStream_t
+ *    passed as void*; NULL = the null stream) and return without
+ *    synchronising. Calls that overlap in time on different streams and
+ *    touch the same output race.
+ *  - Matrices are row-major. An sm_buf describes one buffer: base pointer,
+ *    leading dimension ld (elements between consecutive rows), block_stride
+ *    (elements between consecutive blocks of a stacked layout, or 0 for the
+ *    global layout) and elems (number of elements the buffer holds; every
+ *    access is checked against it on the host).
+ *  - Alignment: base pointers 16-byte aligned; ld and block_stride multiples
+ *    of 8 elements for bfloat16 and of 4 for float32 (SM_ERR_ALIGN).
+ */
+#ifndef SHARDMM_H
+#define SHARDMM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SM_ABI_VERSION 1
+#define SM_MAX_AXES 4
+#define SM_NAME_LEN 8
+
+typedef enum {
+  SM_OK = 0,
+  SM_ERR_ARG = 1,          /* null pointer, bad enum, index or range */
+  SM_ERR_MESH = 2,         /* 0 or > SM_MAX_AXES axes, size < 1, duplicate/empty name */
+  SM_ERR_SPEC = 3,         /* unparsable spec text, unknown axis, > 2 dims */
+  SM_ERR_AXIS_REUSED = 4,  /* one mesh axis shards two dims of one array */
+  SM_ERR_SHAPE = 5,        /* I, J or K < 1; a view larger than its buffer; ld too small */
+  SM_ERR_INDIVISIBLE = 6,  /* a sharded dim does not split evenly; RS rows % N != 0 */
+  SM_ERR_J_MISMATCH = 7,   /* A and B shard J over different axis lists */
+  SM_ERR_NEEDS_GATHER = 8, /* local product asked of a case-2 or case-4 plan */
+  SM_ERR_UNREDUCED = 9,    /* unreduced partials treated as finished blocks */
+  SM_ERR_CASE = 10,        /* operation does not fit the plan's case */
+  SM_ERR_DTYPE = 11,       /* unsupported element type for this operation */
+  SM_ERR_ALIGN = 12,       /* pointer / ld / block_stride alignment */
+  SM_ERR_HIP = 13          /* the HIP runtime reported an error */
+} sm_status;
+
+typedef enum { SM_CASE1 = 1, SM_CASE2 = 2, SM_CASE3 = 3, SM_CASE4 = 4 } sm_case;
+typedef enum { SM_BF16 = 0, SM_F32 = 1 } sm_dtype;
+typedef enum { SM_ALLREDUCE = 0, SM_REDUCESCATTER = 1 } sm_reduce_mode;
+
+/* Epilogue applied to each fp32 accumulator of the local product before it
+ * is stored in the plan's out_dtype (bfloat16 stores round to nearest even).
+ * GeLU is the tanh form 0.5 x (1 + tanh(sqrt(2/pi) (x + 0.044715 x^3))),
+ * applied elementwise to column blocks (ana-alekseeva.com, "MLP block"). */
+typedef enum { SM_EPI_STORE = 0, SM_EPI_GELU_TANH = 1 } sm_epilogue;
+
+/* What sm_gather_shards assembles. */
+typedef enum {
+  SM_WHAT_A = 0,           /* operand A blocks (stacked by A block id) */
+  SM_WHAT_B = 1,           /* operand B blocks (stacked by B block id) */
+  SM_WHAT_C_BLOCKS = 2,    /* finished output blocks, one per group */
+  SM_WHAT_C_SCATTERED = 3, /* reduce-scatter output, one per (group, y) */
+  SM_WHAT_C_PARTIAL = 4    /* unreduced partials: always SM_ERR_UNREDUCED */
+} sm_what;
+
+/* A mesh of named axes, e.g. {X:4, Y:2} = 8 logical ranks. Ranks are
+ * numbered row-major over the axes in declared order. */
+typedef struct {
+  int32_t n_axes;
+  char names[SM_MAX_AXES][SM_NAME_LEN];
+  int32_t sizes[SM_MAX_AXES];
+} sm_mesh;
+
+/* Sharding of a 2-D array: per dimension, the ordered list of mesh axis
+ * indices that split it (first listed = major when flattened). */
+typedef struct {
+  int32_t n[2];
+  int32_t axes[2][SM_MAX_AXES];
+} sm_spec;
+
+/* A plan: caller-owned, immutable once filled by sm_plan.
+ * A "unit" is one distinct local product: unit = g * n_partials + y, with g
+ * the output block (group) index = i_block * c_grid[1] + k_block and y the
+ * index of the rank's J slice (0 unless case 3). Ranks on axes used by
+ * neither operand compute identical units (c_copies of each). */
+typedef struct {
+  uint32_t magic;          /* set by sm_plan; calls reject other values */
+  int32_t kase;            /* sm_case */
+  int32_t n_ranks;
+  int32_t in_dtype;        /* sm_dtype of A and B (bfloat16) */
+  int32_t out_dtype;       /* sm_dtype of the local products */
+  int32_t n_partials;      /* N: partials per output block (1 unless case 3) */
+  int32_t n_groups;        /* G: distinct output blocks */
+  int32_t n_units;         /* G * N */
+  int64_t I, J, K;
+  int64_t a_local[2], b_local[2], c_local[2];
+  int32_t a_grid[2], b_grid[2], c_grid[2];
+  int32_t a_copies, b_copies, c_copies;
+  uint32_t reduce_axes;    /* case 3: bit i set = axis i still to be summed ({U_...}) */
+  int32_t gather_operand;  /* case 2/4: 0 = A, 1 = B; -1 otherwise */
+  uint32_t gather_axes;    /* case 2/4: axes to all-gather that operand over */
+  sm_mesh mesh;
+  sm_spec a, b;
+  sm_spec c;               /* output spec of the local products */
+  sm_spec c_rs;            /* case 3: output spec after reduce-scatter */
+} sm_plan_t;
+
+/* One rank's place in a plan (block indices and global coordinates). */
+typedef struct {
+  int32_t coords[SM_MAX_AXES];
+  int32_t unit, group, partial;   /* -1 when the plan has no local product */
+  int32_t a_block[2], b_block[2], c_block[2];
+  int64_t a_row0, a_col0, b_row0, b_col0, c_row0, c_col0;
+  int64_t rs_row0, rs_rows;       /* case 3: global rows owned after reduce-scatter */
+} sm_rank_info_t;
+
+typedef struct {
+  void* ptr;
+  int64_t ld;
+  int64_t block_stride;
+  int64_t elems;
+} sm_buf;
+
+/* ABI version and the size of sm_plan_t, for bindings to check layouts. */
+int32_t sm_abi_version(void);
+size_t sm_plan_size(void);
+
+/* Human-readable name of a status; thread-local detail of the last error. */
+const char* sm_status_str(int32_t status);
+const char* sm_last_error(void);
+
+/* Fill a mesh from axis names (each 1..SM_NAME_LEN-1 chars) and sizes. */
+int32_t sm_mesh_init(sm_mesh* mesh, int32_t n_axes, const char* const* names,
+                     const int32_t* sizes);
+
+/* Parse a partition spec for a 2-D array (learntpu.dev ch05, Notation
+ * table and the sandbox's accepted forms): "P('X','Y')",
+ * "P(('X','Y'), None)", "P(None, None)", "P()", "('X','Y'), None", or the
+ * subscript notation "A[I_X, J_Y]", "I_XY, J" (single-letter axes). */
+int32_t sm_parse_spec(const sm_mesh* mesh, const char* text, sm_spec* out);
+
+/* Classify A[I,J].B[J,K] on the mesh into the four cases and fill *out
+ * (lingze.zone Case 1-4 and Summary; learntpu.dev ch05 "The four cases").
+ * Checks, in order: mesh, specs (SM_ERR_SPEC, SM_ERR_AXIS_REUSED), shape
+ * (SM_ERR_SHAPE), divisibility (SM_ERR_INDIVISIBLE); then case 4 (A's I
+ * and B's K share an axis) before the J cases; J sharded by both on
+ * different axis lists is SM_ERR_J_MISMATCH. in_dtype must be SM_BF16;
+ * out_dtype SM_F32, or SM_BF16 when no partial sums arise (not case 3). */
+int32_t sm_plan(const sm_mesh* mesh, const sm_spec* a, const sm_spec* b,
+                int64_t I, int64_t J, int64_t K, int32_t in_dtype,
+                int32_t out_dtype, sm_plan_t* out);
+
+/* Where rank `rank` sits in the plan. */
+int32_t sm_rank_info(const sm_plan_t* plan, int32_t rank, sm_rank_info_t* out);
+
+/* Local products C_u = A_u . B_u for units [unit_begin, unit_begin+count):
+ * bfloat16 inputs, fp32 accumulation, epilogue, store in plan->out_dtype
+ * (learntpu.dev ch05 sandbox "Local matmul"; lingze.zone Case 1 and 3).
+ *  A, B: global layout (block_stride 0: the unit's view is taken at its
+ *        block coordinates in the whole [I,J] / [J,K] array) or stacked
+ *        (block_stride > 0: block id = row_block * grid[1] + col_block).
+ *  C:    case 1: global layout (the [I,K] array) or stacked; case 3:
+ *        stacked only (partials overlap in output coordinates, so a global
+ *        layout is SM_ERR_UNREDUCED). Stacked output blocks are indexed
+ *        relative to unit_begin.
+ * Rows of at most 16 (a skinny batch) use a split-J streaming kernel; other
+ * shapes use the LDS-tiled MFMA kernel. Errors: SM_ERR_NEEDS_GATHER for
+ * case 2/4, SM_ERR_CASE for a GeLU epilogue on case 3. */
+int32_t sm_local_gemm(const sm_plan_t* plan, const sm_buf* A, const sm_buf* B,
+                      const sm_buf* C, int32_t epilogue, int32_t unit_begin,
+                      int32_t unit_count, void* stream);
+
+/* Sum the N partials of each group g in [group_begin, group_begin+count)
+ * in rank order in fp32: S_g = (((P_{g,0} + P_{g,1}) + ...) + P_{g,N-1})
+ * (semiaifoundry.com "The mechanism" step 4; learntpu.dev ch05 table of
+ * the four collectives).
+ *  partials: stacked fp32, block index = unit - group_begin * N.
+ *  SM_ALLREDUCE: out receives S_g, one copy per group (every rank of the
+ *    group shares it): global [I,K] layout (block_stride 0) or stacked by
+ *    g - group_begin.
+ *  SM_REDUCESCATTER: reduce coordinate y keeps rows [y m/N, (y+1) m/N) of
+ *    S_g: global layout (rows at the plan's c_rs coordinates) or stacked by
+ *    (g - group_begin) * N + y, each block [m/N, n].
+ * Errors: SM_ERR_CASE unless case 3; SM_ERR_INDIVISIBLE if RS and m % N. */
+int32_t sm_reduce_partials(const sm_plan_t* plan, const sm_buf* partials,
+                           const sm_buf* out, int32_t mode, int32_t group_begin,
+                           int32_t group_count, void* stream);
+
+/* All-gather on one GPU: copy each distinct finished block once from a
+ * stacked layout into the global layout (lingze.zone Case 1, replication
+ * as a separate AllGather; semiaifoundry.com step 5). what = SM_WHAT_A /
+ * SM_WHAT_B (bfloat16 operand blocks), SM_WHAT_C_BLOCKS (one block per
+ * group: case-1 outputs or all-reduced case-3 outputs), SM_WHAT_C_SCATTERED
+ * (reduce-scatter outputs). SM_WHAT_C_PARTIAL is refused with
+ * SM_ERR_UNREDUCED: concatenating partials does not add them. out must use
+ * the global layout (block_stride 0). */
+int32_t sm_gather_shards(const sm_plan_t* plan, int32_t what, const sm_buf* shards,
+                         const sm_buf* out, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SHARDMM_H */

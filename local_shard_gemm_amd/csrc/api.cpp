@@ -1,0 +1,350 @@
+// Device entry points of libshardmm: sm_local_gemm, sm_reduce_partials,
+// sm_gather_shards. Every argument is validated on the host before the
+// first HIP call, so a failed check leaves all outputs untouched and makes
+// no device call at all.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "internal.h"
+#include "kernels.h"
+
+namespace shardmm {
+namespace {
+
+// Describes how one logical block of a buffer is addressed.
+struct BlockRef {
+  int64_t offset;  // element offset of the block's (0,0)
+  int64_t rows, cols;
+};
+
+int32_t check_buf_basic(const sm_buf* b, const char* what, int32_t dtype) {
+  if (!b) return fail(SM_ERR_ARG, std::string(what) + ": NULL sm_buf");
+  if (!b->ptr) return fail(SM_ERR_ARG, std::string(what) + ": NULL pointer");
+  if (reinterpret_cast<uintptr_t>(b->ptr) % 16)
+    return fail(SM_ERR_ALIGN, std::string(what) + ": pointer not 16-byte aligned");
+  const int64_t q = dtype == SM_BF16 ? 8 : 4;
+  if (b->ld < 1) return fail(SM_ERR_SHAPE, std::string(what) + ": ld < 1");
+  if (b->ld % q) return fail(SM_ERR_ALIGN, std::string(what) + ": ld not a multiple of " + std::to_string(q));
+  if (b->block_stride < 0) return fail(SM_ERR_ARG, std::string(what) + ": negative block_stride");
+  if (b->block_stride % q)
+    return fail(SM_ERR_ALIGN, std::string(what) + ": block_stride not a multiple of " + std::to_string(q));
+  if (b->elems < 1) return fail(SM_ERR_SHAPE, std::string(what) + ": elems < 1");
+  return SM_OK;
+}
+
+// A block at `offset` spanning rows x cols must lie inside the buffer.
+int32_t check_extent(const sm_buf* b, const BlockRef& r, const char* what) {
+  if (r.cols > b->ld) return fail(SM_ERR_SHAPE, std::string(what) + ": ld smaller than the block width");
+  const int64_t last = r.offset + (r.rows - 1) * b->ld + r.cols;
+  if (r.offset < 0 || last > b->elems)
+    return fail(SM_ERR_SHAPE, std::string(what) + ": block extends past the buffer (" + std::to_string(last) +
+                                  " > " + std::to_string(b->elems) + " elements)");
+  return SM_OK;
+}
+
+// Stacked layout: blocks must not overlap (required of outputs, harmless
+// for inputs but kept uniform).
+int32_t check_stacked(const sm_buf* b, int64_t rows, int64_t cols, const char* what) {
+  if (cols > b->ld) return fail(SM_ERR_SHAPE, std::string(what) + ": ld smaller than the block width");
+  if (b->block_stride < rows * b->ld)
+    return fail(SM_ERR_SHAPE, std::string(what) + ": block_stride smaller than rows * ld");
+  return SM_OK;
+}
+
+int32_t hip_fail(hipError_t e, const char* where) {
+  return fail(SM_ERR_HIP, std::string(where) + ": " + hipGetErrorString(e));
+}
+
+}  // namespace
+}  // namespace shardmm
+
+using namespace shardmm;
+
+extern "C" int32_t sm_local_gemm(const sm_plan_t* plan, const sm_buf* A, const sm_buf* B, const sm_buf* C,
+                                 int32_t epilogue, int32_t unit_begin, int32_t unit_count, void* stream) {
+  clear_error();
+  int32_t st = check_plan(plan);
+  if (st) return st;
+  const sm_plan_t& p = *plan;
+  if (p.kase == SM_CASE2 || p.kase == SM_CASE4)
+    return fail(SM_ERR_NEEDS_GATHER, std::string("case ") + std::to_string(p.kase) + ": all-gather operand " +
+                                         (p.gather_operand == 0 ? "A" : "B") + " first");
+  if (p.kase != SM_CASE1 && p.kase != SM_CASE3) return fail(SM_ERR_ARG, "corrupt plan");
+  if (epilogue != SM_EPI_STORE && epilogue != SM_EPI_GELU_TANH) return fail(SM_ERR_ARG, "unknown epilogue");
+  if (epilogue == SM_EPI_GELU_TANH && p.kase == SM_CASE3)
+    return fail(SM_ERR_CASE, "GeLU of an unreduced partial is not GeLU of the sum");
+  if (p.in_dtype != SM_BF16) return fail(SM_ERR_DTYPE, "inputs must be bfloat16");
+  if (unit_count < 1 || unit_begin < 0 || unit_begin > p.n_units - unit_count)
+    return fail(SM_ERR_ARG, "unit range outside [0, n_units)");
+  if ((st = check_buf_basic(A, "A", SM_BF16))) return st;
+  if ((st = check_buf_basic(B, "B", SM_BF16))) return st;
+  if ((st = check_buf_basic(C, "C", p.out_dtype))) return st;
+  if (p.kase == SM_CASE3 && C->block_stride == 0)
+    return fail(SM_ERR_UNREDUCED, "case-3 partials overlap in output coordinates; C must be stacked");
+
+  const int64_t m = p.a_local[0], k = p.a_local[1], n = p.b_local[1];
+  if (m > INT32_MAX / 2 || n > INT32_MAX / 2 || k > INT32_MAX / 2) return fail(SM_ERR_SHAPE, "local shape too large");
+  if (A->block_stride == 0 && A->ld < p.J) return fail(SM_ERR_SHAPE, "A: global layout needs ld >= J");
+  if (B->block_stride == 0 && B->ld < p.K) return fail(SM_ERR_SHAPE, "B: global layout needs ld >= K");
+  if (C->block_stride == 0 && C->ld < p.K) return fail(SM_ERR_SHAPE, "C: global layout needs ld >= K");
+  if (A->block_stride > 0 && (st = check_stacked(A, m, k, "A"))) return st;
+  if (B->block_stride > 0 && (st = check_stacked(B, k, n, "B"))) return st;
+  if (C->block_stride > 0 && (st = check_stacked(C, m, n, "C"))) return st;
+
+  struct Item {
+    int32_t unit, b_id, a_row;
+    GemmUnitPtrs ptrs;
+  };
+  std::vector<Item> items;
+  items.reserve(unit_count);
+  const size_t csz = dtype_size(p.out_dtype);
+  for (int32_t u = unit_begin; u < unit_begin + unit_count; ++u) {
+    UnitView v;
+    if ((st = unit_view(p, u, &v))) return st;
+    BlockRef ra, rb, rc;
+    ra.rows = m;
+    ra.cols = k;
+    rb.rows = k;
+    rb.cols = n;
+    rc.rows = m;
+    rc.cols = n;
+    const int32_t a_id = v.a_block[0] * p.a_grid[1] + v.a_block[1];
+    const int32_t b_id = v.b_block[0] * p.b_grid[1] + v.b_block[1];
+    ra.offset = A->block_stride ? a_id * A->block_stride : v.a_row0 * A->ld + v.a_col0;
+    rb.offset = B->block_stride ? b_id * B->block_stride : v.b_row0 * B->ld + v.b_col0;
+    rc.offset = C->block_stride ? static_cast<int64_t>(u - unit_begin) * C->block_stride : v.c_row0 * C->ld + v.c_col0;
+    if ((st = check_extent(A, ra, "A"))) return st;
+    if ((st = check_extent(B, rb, "B"))) return st;
+    if ((st = check_extent(C, rc, "C"))) return st;
+    Item it;
+    it.unit = u;
+    it.b_id = b_id;
+    it.a_row = v.a_block[0];
+    it.ptrs.a = static_cast<const uint16_t*>(A->ptr) + ra.offset;
+    it.ptrs.b = static_cast<const uint16_t*>(B->ptr) + rb.offset;
+    it.ptrs.c = static_cast<char*>(C->ptr) + rc.offset * static_cast<int64_t>(csz);
+    items.push_back(it);
+  }
+  // Units sharing a B block go next to each other (their tiles stack into
+  // one tall matrix in the kernel's tile order).
+  std::stable_sort(items.begin(), items.end(), [](const Item& x, const Item& y) {
+    return x.b_id != y.b_id ? x.b_id < y.b_id : x.a_row < y.a_row;
+  });
+
+  GemmLaunch L;
+  std::memset(&L, 0, sizeof L);
+  L.M = static_cast<int32_t>(m);
+  L.N = static_cast<int32_t>(n);
+  L.K = static_cast<int32_t>(k);
+  L.tiles_m = static_cast<int32_t>((m + kTileM - 1) / kTileM);
+  L.tiles_n = static_cast<int32_t>((n + kTileN - 1) / kTileN);
+  L.lda = A->ld;
+  L.ldb = B->ld;
+  L.ldc = C->ld;
+  L.epilogue = epilogue == SM_EPI_GELU_TANH ? kEpiGelu : kEpiStore;
+  L.out_bf16 = p.out_dtype == SM_BF16 ? 1 : 0;
+  L.vec_ok = 1;
+  for (const Item& it : items)
+    if (reinterpret_cast<uintptr_t>(it.ptrs.a) % 16 || reinterpret_cast<uintptr_t>(it.ptrs.b) % 16) L.vec_ok = 0;
+  const bool skinny = m <= kSkinnyMaxM;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  for (size_t first = 0; first < items.size(); first += kMaxUnitsPerLaunch) {
+    const size_t cnt = std::min(items.size() - first, static_cast<size_t>(kMaxUnitsPerLaunch));
+    L.n_units = static_cast<int32_t>(cnt);
+    for (size_t i = 0; i < cnt; ++i) L.u[i] = items[first + i].ptrs;
+    hipError_t e = skinny ? launch_gemm_skinny(L, s) : launch_gemm_mfma(L, s);
+    if (e != hipSuccess) return hip_fail(e, "sm_local_gemm launch");
+  }
+  return SM_OK;
+}
+
+namespace {
+
+// 16-byte vectors need aligned row starts in every source and the target.
+void set_vec_flags(std::vector<RowJob>& jobs, int32_t elem_bytes) {
+  const int64_t per = 16 / elem_bytes;
+  for (RowJob& J : jobs) {
+    const bool ok = reinterpret_cast<uintptr_t>(J.src) % 16 == 0 && reinterpret_cast<uintptr_t>(J.dst) % 16 == 0 &&
+                    J.lds % per == 0 && J.ldd % per == 0 && J.src_stride % per == 0 && J.cols % per == 0;
+    J.vec = ok ? 1 : 0;
+  }
+}
+
+int32_t run_jobs(std::vector<RowJob>& jobs, int32_t n_sum, int32_t elem_bytes, hipStream_t s, const char* where) {
+  set_vec_flags(jobs, elem_bytes);
+  RowLaunch L;
+  for (size_t first = 0; first < jobs.size(); first += kMaxJobsPerLaunch) {
+    std::memset(&L, 0, sizeof L);
+    const size_t cnt = std::min(jobs.size() - first, static_cast<size_t>(kMaxJobsPerLaunch));
+    L.n_jobs = static_cast<int32_t>(cnt);
+    L.n_sum = n_sum;
+    L.elem_bytes = elem_bytes;
+    L.max_rows = 0;
+    for (size_t i = 0; i < cnt; ++i) {
+      L.jobs[i] = jobs[first + i];
+      L.max_rows = std::max(L.max_rows, L.jobs[i].rows);
+    }
+    hipError_t e = launch_rows(L, s);
+    if (e != hipSuccess) return hip_fail(e, where);
+  }
+  return SM_OK;
+}
+
+}  // namespace
+
+extern "C" int32_t sm_reduce_partials(const sm_plan_t* plan, const sm_buf* partials, const sm_buf* out,
+                                      int32_t mode, int32_t group_begin, int32_t group_count, void* stream) {
+  clear_error();
+  int32_t st = check_plan(plan);
+  if (st) return st;
+  const sm_plan_t& p = *plan;
+  if (p.kase != SM_CASE3) return fail(SM_ERR_CASE, "only case-3 plans have partial sums to reduce");
+  if (mode != SM_ALLREDUCE && mode != SM_REDUCESCATTER) return fail(SM_ERR_ARG, "unknown reduce mode");
+  if (p.out_dtype != SM_F32) return fail(SM_ERR_DTYPE, "partials are float32");
+  if (group_count < 1 || group_begin < 0 || group_begin > p.n_groups - group_count)
+    return fail(SM_ERR_ARG, "group range outside [0, n_groups)");
+  if ((st = check_buf_basic(partials, "partials", SM_F32))) return st;
+  if ((st = check_buf_basic(out, "out", SM_F32))) return st;
+  if (partials->block_stride == 0)
+    return fail(SM_ERR_UNREDUCED, "partials overlap in output coordinates; they must be stacked");
+  const int64_t m = p.c_local[0], n = p.c_local[1];
+  const int32_t N = p.n_partials;
+  if (m > INT32_MAX || n > INT32_MAX) return fail(SM_ERR_SHAPE, "block too large");
+  if ((st = check_stacked(partials, m, n, "partials"))) return st;
+  {
+    BlockRef last{static_cast<int64_t>(group_count) * N * partials->block_stride - partials->block_stride, m, n};
+    if ((st = check_extent(partials, last, "partials"))) return st;
+  }
+  const bool rs = mode == SM_REDUCESCATTER;
+  if (rs && m % N) return fail(SM_ERR_INDIVISIBLE, "rows of a block do not split N ways");
+  const int64_t orows = rs ? m / N : m;
+  if (out->block_stride == 0) {
+    if (out->ld < p.K) return fail(SM_ERR_SHAPE, "out: global layout needs ld >= K");
+  } else if ((st = check_stacked(out, orows, n, "out"))) {
+    return st;
+  }
+
+  std::vector<RowJob> jobs;
+  const float* P = static_cast<const float*>(partials->ptr);
+  float* O = static_cast<float*>(out->ptr);
+  for (int32_t g = group_begin; g < group_begin + group_count; ++g) {
+    const int64_t bi = g / p.c_grid[1], bk = g % p.c_grid[1];
+    const int64_t src0 = static_cast<int64_t>(g - group_begin) * N * partials->block_stride;
+    const int32_t nblk = rs ? N : 1;
+    for (int32_t y = 0; y < nblk; ++y) {
+      BlockRef d;
+      d.rows = orows;
+      d.cols = n;
+      if (out->block_stride == 0)
+        d.offset = (bi * m + y * orows) * out->ld + bk * n;
+      else
+        d.offset = (static_cast<int64_t>(g - group_begin) * nblk + y) * out->block_stride;
+      if ((st = check_extent(out, d, "out"))) return st;
+      RowJob J;
+      J.src = P + src0 + y * orows * partials->ld;
+      J.dst = O + d.offset;
+      J.src_stride = partials->block_stride;
+      J.lds = partials->ld;
+      J.ldd = out->ld;
+      J.rows = static_cast<int32_t>(orows);
+      J.cols = static_cast<int32_t>(n);
+      jobs.push_back(J);
+    }
+  }
+  return run_jobs(jobs, N, 4, static_cast<hipStream_t>(stream), "sm_reduce_partials launch");
+}
+
+extern "C" int32_t sm_gather_shards(const sm_plan_t* plan, int32_t what, const sm_buf* shards, const sm_buf* out,
+                                    void* stream) {
+  clear_error();
+  int32_t st = check_plan(plan);
+  if (st) return st;
+  const sm_plan_t& p = *plan;
+  if (what == SM_WHAT_C_PARTIAL)
+    return fail(SM_ERR_UNREDUCED, "concatenating unreduced partials does not add them; reduce first");
+  if (what < SM_WHAT_A || what > SM_WHAT_C_SCATTERED) return fail(SM_ERR_ARG, "unknown sm_what");
+  if ((what == SM_WHAT_C_BLOCKS) && p.kase != SM_CASE1 && p.kase != SM_CASE3)
+    return fail(SM_ERR_CASE, "no local output blocks in a case-2/4 plan");
+  if (what == SM_WHAT_C_SCATTERED && p.kase != SM_CASE3)
+    return fail(SM_ERR_CASE, "reduce-scatter blocks exist only for case 3");
+
+  int32_t dtype;
+  int64_t rows, cols, grid_r, grid_c, gwidth;
+  switch (what) {
+    case SM_WHAT_A:
+      dtype = p.in_dtype;
+      rows = p.a_local[0];
+      cols = p.a_local[1];
+      grid_r = p.a_grid[0];
+      grid_c = p.a_grid[1];
+      gwidth = p.J;
+      break;
+    case SM_WHAT_B:
+      dtype = p.in_dtype;
+      rows = p.b_local[0];
+      cols = p.b_local[1];
+      grid_r = p.b_grid[0];
+      grid_c = p.b_grid[1];
+      gwidth = p.K;
+      break;
+    case SM_WHAT_C_BLOCKS:
+      dtype = p.out_dtype;
+      rows = p.c_local[0];
+      cols = p.c_local[1];
+      grid_r = p.c_grid[0];
+      grid_c = p.c_grid[1];
+      gwidth = p.K;
+      break;
+    default:  // SM_WHAT_C_SCATTERED
+      if (p.c_local[0] % p.n_partials) return fail(SM_ERR_INDIVISIBLE, "rows of a block do not split N ways");
+      dtype = p.out_dtype;
+      rows = p.c_local[0] / p.n_partials;
+      cols = p.c_local[1];
+      grid_r = static_cast<int64_t>(p.c_grid[0]) * p.n_partials;
+      grid_c = p.c_grid[1];
+      gwidth = p.K;
+      break;
+  }
+  if (rows > INT32_MAX || cols > INT32_MAX) return fail(SM_ERR_SHAPE, "block too large");
+  if ((st = check_buf_basic(shards, "shards", dtype))) return st;
+  if ((st = check_buf_basic(out, "out", dtype))) return st;
+  if (shards->block_stride == 0) return fail(SM_ERR_ARG, "shards must use the stacked layout");
+  if (out->block_stride != 0) return fail(SM_ERR_ARG, "out must use the global layout");
+  if (out->ld < gwidth) return fail(SM_ERR_SHAPE, "out: ld smaller than the global width");
+  if ((st = check_stacked(shards, rows, cols, "shards"))) return st;
+
+  // Stacked order of blocks: for C_SCATTERED the (group, y) index, which is
+  // the row-block index (bi * N + y) when the grid has one block column;
+  // in general block id = (g * N + y) with g = bi * grid_c + bk.
+  std::vector<RowJob> jobs;
+  const size_t esz = dtype_size(dtype);
+  for (int64_t id = 0; id < grid_r * grid_c; ++id) {
+    int64_t r0, c0;
+    if (what == SM_WHAT_C_SCATTERED) {
+      const int64_t g = id / p.n_partials, y = id % p.n_partials;
+      r0 = (g / p.c_grid[1]) * p.c_local[0] + y * rows;
+      c0 = (g % p.c_grid[1]) * cols;
+    } else {
+      r0 = (id / grid_c) * rows;
+      c0 = (id % grid_c) * cols;
+    }
+    BlockRef s{id * shards->block_stride, rows, cols};
+    BlockRef d{r0 * out->ld + c0, rows, cols};
+    if ((st = check_extent(shards, s, "shards"))) return st;
+    if ((st = check_extent(out, d, "out"))) return st;
+    RowJob J;
+    J.src = static_cast<const char*>(shards->ptr) + s.offset * static_cast<int64_t>(esz);
+    J.dst = static_cast<char*>(out->ptr) + d.offset * static_cast<int64_t>(esz);
+    J.src_stride = 0;
+    J.lds = shards->ld;
+    J.ldd = out->ld;
+    J.rows = static_cast<int32_t>(rows);
+    J.cols = static_cast<int32_t>(cols);
+    jobs.push_back(J);
+  }
+  return run_jobs(jobs, 1, static_cast<int32_t>(esz), static_cast<hipStream_t>(stream), "sm_gather_shards launch");
+}

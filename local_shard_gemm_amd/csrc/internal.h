@@ -1,0 +1,34 @@
+// Internal declarations shared by the library's translation units.
+#pragma once
+
+#include <cstdint>
+#include <string>
+
+#include "shardmm.h"
+
+namespace shardmm {
+
+constexpr uint32_t kPlanMagic = 0x5348414Du;  // "SHAM"
+
+// Record a failure and return its status (thread-local text for sm_last_error).
+int32_t fail(int32_t status, const std::string& msg);
+void clear_error();
+
+// Flattened block index of `coords` over an ordered axis list (first = major).
+int32_t block_of(const sm_mesh& mesh, const int32_t* axes, int32_t n, const int32_t* coords);
+int32_t axes_product(const sm_mesh& mesh, const int32_t* axes, int32_t n);
+void rank_coords(const sm_mesh& mesh, int32_t rank, int32_t* coords);
+
+// Global coordinates of one unit's operand and output views.
+struct UnitView {
+  int32_t a_block[2], b_block[2], c_block[2];
+  int64_t a_row0, a_col0, b_row0, b_col0, c_row0, c_col0;
+  int32_t group, partial;
+};
+int32_t unit_view(const sm_plan_t& p, int32_t unit, UnitView* out);
+
+int32_t check_plan(const sm_plan_t* p);
+
+size_t dtype_size(int32_t dt);
+
+}  // namespace shardmm

@@ -1,0 +1,62 @@
+// Launch descriptors of libshardmm's device kernels. Everything here is
+// passed by value as kernel arguments (no device-side tables, no workspace).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace shardmm {
+
+constexpr int kMaxUnitsPerLaunch = 64;
+constexpr int kMaxJobsPerLaunch = 32;
+
+// One local product: pointers already offset to the unit's views.
+struct GemmUnitPtrs {
+  const uint16_t* a;  // [M, K] bfloat16, leading dim lda
+  const uint16_t* b;  // [K, N] bfloat16, leading dim ldb
+  void* c;            // [M, N] float32 or bfloat16, leading dim ldc
+};
+
+enum : int32_t { kEpiStore = 0, kEpiGelu = 1 };
+
+struct GemmLaunch {
+  int32_t M, N, K;           // local shape shared by all units of the launch
+  int32_t tiles_m, tiles_n;  // MFMA kernel only
+  int32_t n_units;
+  int64_t lda, ldb, ldc;
+  int32_t epilogue;          // kEpiStore / kEpiGelu
+  int32_t out_bf16;          // 1: store bfloat16 (RNE), 0: float32
+  int32_t vec_ok;            // 1: every A/B view starts 16-byte aligned
+  GemmUnitPtrs u[kMaxUnitsPerLaunch];  // in scheduling order
+};
+
+// Rank-order sum / copy of row blocks: dst[r, c] = sum_{y<N} src_y[r, c]
+// with src_y = src + y * src_stride (elements).
+struct RowJob {
+  const void* src;
+  void* dst;
+  int64_t src_stride;
+  int64_t lds, ldd;
+  int32_t rows, cols;
+  int32_t vec;  // 1: src, dst, lds, ldd and src_stride allow 16-byte vectors
+};
+
+struct RowLaunch {
+  int32_t n_jobs;
+  int32_t n_sum;       // N (1 = plain copy)
+  int32_t elem_bytes;  // 4 (float32 sum / copy) or 2 (bfloat16 copy)
+  int32_t max_rows;
+  RowJob jobs[kMaxJobsPerLaunch];
+};
+
+hipError_t launch_gemm_mfma(const GemmLaunch& L, hipStream_t s);
+hipError_t launch_gemm_skinny(const GemmLaunch& L, hipStream_t s);
+hipError_t launch_rows(const RowLaunch& L, hipStream_t s);
+
+// Tile sizes of the MFMA kernel (host side uses them for the grid).
+constexpr int kTileM = 256, kTileN = 256, kTileK = 64;
+// Rows handled by the skinny split-J kernel.
+constexpr int kSkinnyMaxM = 16;
+
+}  // namespace shardmm

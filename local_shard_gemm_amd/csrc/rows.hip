@@ -1,0 +1,160 @@
+// Streaming row kernel behind sm_reduce_partials and sm_gather_shards.
+//
+//  * Reduce (n_sum = N >= 2, float32): dst[r, c] = (((P_0 + P_1) + P_2) ...)
+//    [r, c], the partials added in rank order -- the addition of
+//    contributions with matching output coordinates that finishes a case-3
+//    product (semiaifoundry.com "The mechanism", step 4; learntpu.dev ch05,
+//    AllReduce / ReduceScatter rows of the collectives table). With all
+//    ranks on one GPU the "collective" is this HBM-bound pass.
+//  * Copy (n_sum = 1): all-gather of finished blocks into the global layout.
+//
+// Design (gfx950): pure streaming. Each workgroup owns one row of one job;
+// its 256 threads walk the row in 16-byte vectors, four vectors per thread
+// per iteration, and issue every partial's loads before the rank-ordered
+// adds so that 4 x N loads per thread are in flight. Loads and stores are
+// non-temporal: nothing is re-read, so the data should not displace L2.
+#include "kernels.h"
+
+namespace shardmm {
+namespace {
+
+constexpr int NT = 256;
+constexpr int UNROLL = 4;
+
+__device__ __forceinline__ float4 ldnt(const float4* p) {
+  float4 v;
+  v.x = __builtin_nontemporal_load(&p->x);
+  v.y = __builtin_nontemporal_load(&p->y);
+  v.z = __builtin_nontemporal_load(&p->z);
+  v.w = __builtin_nontemporal_load(&p->w);
+  return v;
+}
+
+__device__ __forceinline__ void stnt(float4* p, const float4& v) {
+  __builtin_nontemporal_store(v.x, &p->x);
+  __builtin_nontemporal_store(v.y, &p->y);
+  __builtin_nontemporal_store(v.z, &p->z);
+  __builtin_nontemporal_store(v.w, &p->w);
+}
+
+__device__ __forceinline__ void add4(float4& a, const float4& b) {
+  a.x += b.x;
+  a.y += b.y;
+  a.z += b.z;
+  a.w += b.w;
+}
+
+// Rank-ordered sum of NS partials (NS > 0 fixed at compile time, or the
+// runtime count when NS == 0) for one row, float4 path.
+template <int NS>
+__device__ __forceinline__ void sum_row_vec(const RowJob& J, int n_sum, int row) {
+  const int nsum = NS > 0 ? NS : n_sum;
+  const float* src = static_cast<const float*>(J.src) + static_cast<int64_t>(row) * J.lds;
+  float* dst = static_cast<float*>(J.dst) + static_cast<int64_t>(row) * J.ldd;
+  const int n4 = J.cols >> 2;
+  for (int base = threadIdx.x; base < n4; base += NT * UNROLL) {
+    float4 acc[UNROLL];
+    if (NS > 0) {
+      float4 v[NS > 0 ? NS : 1][UNROLL];
+#pragma unroll
+      for (int y = 0; y < (NS > 0 ? NS : 1); ++y)
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u) {
+          const int c4 = base + u * NT;
+          if (c4 < n4)
+            v[y][u] = ldnt(reinterpret_cast<const float4*>(src + y * J.src_stride) + c4);
+        }
+#pragma unroll
+      for (int u = 0; u < UNROLL; ++u) {
+        acc[u] = v[0][u];
+#pragma unroll
+        for (int y = 1; y < (NS > 0 ? NS : 1); ++y) add4(acc[u], v[y][u]);
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < UNROLL; ++u) {
+        const int c4 = base + u * NT;
+        if (c4 < n4) acc[u] = ldnt(reinterpret_cast<const float4*>(src) + c4);
+      }
+      for (int y = 1; y < nsum; ++y) {
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u) {
+          const int c4 = base + u * NT;
+          if (c4 < n4) add4(acc[u], ldnt(reinterpret_cast<const float4*>(src + y * J.src_stride) + c4));
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < UNROLL; ++u) {
+      const int c4 = base + u * NT;
+      if (c4 < n4) stnt(reinterpret_cast<float4*>(dst) + c4, acc[u]);
+    }
+  }
+}
+
+__device__ __forceinline__ void sum_row_scalar(const RowJob& J, int n_sum, int row) {
+  const float* src = static_cast<const float*>(J.src) + static_cast<int64_t>(row) * J.lds;
+  float* dst = static_cast<float*>(J.dst) + static_cast<int64_t>(row) * J.ldd;
+  for (int c = threadIdx.x; c < J.cols; c += NT) {
+    float s = src[c];
+    for (int y = 1; y < n_sum; ++y) s += src[y * J.src_stride + c];
+    dst[c] = s;
+  }
+}
+
+__device__ __forceinline__ void copy_row_16(const RowJob& J, int row) {
+  // 16-bit elements; 8 per 16-byte vector (alignment checked by the host).
+  const uint16_t* src = static_cast<const uint16_t*>(J.src) + static_cast<int64_t>(row) * J.lds;
+  uint16_t* dst = static_cast<uint16_t*>(J.dst) + static_cast<int64_t>(row) * J.ldd;
+  const int n8 = J.cols >> 3;
+  for (int c = threadIdx.x; c < n8; c += NT)
+    reinterpret_cast<uint4*>(dst)[c] = reinterpret_cast<const uint4*>(src)[c];
+}
+
+__device__ __forceinline__ void copy_row_16_scalar(const RowJob& J, int row) {
+  const uint16_t* src = static_cast<const uint16_t*>(J.src) + static_cast<int64_t>(row) * J.lds;
+  uint16_t* dst = static_cast<uint16_t*>(J.dst) + static_cast<int64_t>(row) * J.ldd;
+  for (int c = threadIdx.x; c < J.cols; c += NT) dst[c] = src[c];
+}
+
+template <int NS>
+__global__ __launch_bounds__(NT) void rows_f32_kernel(const RowLaunch L) {
+  const RowJob& J = L.jobs[blockIdx.y];
+  const int row = blockIdx.x;
+  if (row >= J.rows) return;
+  if (J.vec)
+    sum_row_vec<NS>(J, L.n_sum, row);
+  else
+    sum_row_scalar(J, L.n_sum, row);
+}
+
+__global__ __launch_bounds__(NT) void rows_b16_copy_kernel(const RowLaunch L) {
+  const RowJob& J = L.jobs[blockIdx.y];
+  const int row = blockIdx.x;
+  if (row >= J.rows) return;
+  if (J.vec)
+    copy_row_16(J, row);
+  else
+    copy_row_16_scalar(J, row);
+}
+
+}  // namespace
+
+hipError_t launch_rows(const RowLaunch& L, hipStream_t s) {
+  if (L.n_jobs <= 0 || L.max_rows <= 0) return hipSuccess;
+  dim3 grid(L.max_rows, L.n_jobs);
+  if (L.elem_bytes == 2) {
+    hipLaunchKernelGGL(rows_b16_copy_kernel, grid, dim3(NT), 0, s, L);
+  } else {
+    switch (L.n_sum) {
+      case 1: hipLaunchKernelGGL(rows_f32_kernel<1>, grid, dim3(NT), 0, s, L); break;
+      case 2: hipLaunchKernelGGL(rows_f32_kernel<2>, grid, dim3(NT), 0, s, L); break;
+      case 4: hipLaunchKernelGGL(rows_f32_kernel<4>, grid, dim3(NT), 0, s, L); break;
+      case 8: hipLaunchKernelGGL(rows_f32_kernel<8>, grid, dim3(NT), 0, s, L); break;
+      default: hipLaunchKernelGGL(rows_f32_kernel<0>, grid, dim3(NT), 0, s, L); break;
+    }
+  }
+  return hipGetLastError();
+}
+
+}  // namespace shardmm

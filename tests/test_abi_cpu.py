@@ -1,0 +1,253 @@
+"""C-ABI library checks that need no GPU: symbols, plan layout, the host
+planner against the oracle's independent planner, and argument validation
+(every check runs before any HIP call, so no device is touched)."""
+import ctypes
+import itertools
+import os
+import re
+
+import pytest
+
+import local_shard_gemm_amd as sm
+from oracle import planner as ref_planner
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "shardmm.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sm_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = sm.load()
+    names = _declared_functions()
+    assert "sm_plan" in names and "sm_local_gemm" in names
+    for name in names:
+        assert hasattr(lib, name), name
+    assert set(names) == set(sm.EXPORTED)
+
+
+def test_plan_struct_layout_matches():
+    lib = sm.load()
+    assert lib.sm_plan_size() == ctypes.sizeof(sm.sm_plan_t)
+    assert lib.sm_abi_version() == sm.SM_ABI_VERSION
+
+
+def test_status_strings():
+    assert sm.sm_status_str(sm.SM_ERR_UNREDUCED) == "SM_ERR_UNREDUCED"
+    assert sm.sm_status_str(0) == "SM_OK"
+
+
+# ---------------------------------------------------------- spec parsing
+
+@pytest.mark.parametrize("text,dims", [
+    ("P('X', 'Y')", ((0,), (1,))),
+    ("P(('X', 'Y'), None)", ((0, 1), ())),
+    ("P(None, None)", ((), ())),
+    ("P()", ((), ())),
+    ("('X','Y'), None", ((0, 1), ())),
+    ("P('Y', None)", ((1,), ())),
+    ("A[I_X, J_Y]", ((0,), (1,))),
+    ("A[I_XY, J]", ((0, 1), ())),
+    ("I, J_Y", ((), (1,))),
+    ("", ((), ())),
+])
+def test_parse_spec_forms(text, dims):
+    mesh = sm.sm_mesh_init({"X": 4, "Y": 2})
+    assert sm.sm_parse_spec(mesh, text).dims() == dims
+    assert ref_planner.parse_spec(text) == tuple(tuple("XY"[i] for i in d) for d in dims)
+
+
+@pytest.mark.parametrize("text,code", [
+    ("P('X', 'Y', 'X')", sm.SM_ERR_SPEC),
+    ("P('Q', None)", sm.SM_ERR_SPEC),
+    ("P('X'", sm.SM_ERR_SPEC),
+    ("A[I_Q, J]", sm.SM_ERR_SPEC),
+])
+def test_parse_spec_errors(text, code):
+    mesh = sm.sm_mesh_init({"X": 4, "Y": 2})
+    with pytest.raises(sm.ShardmmError) as ei:
+        sm.sm_parse_spec(mesh, text)
+    assert ei.value.status == code
+
+
+def test_mesh_errors():
+    for axes in ({}, {"X": 0}, [("X", 2), ("X", 2)], {"A": 1, "B": 1, "C": 1, "D": 1, "E": 1}, {"TOOLONGNAME": 2}):
+        with pytest.raises(sm.ShardmmError) as ei:
+            sm.sm_mesh_init(axes)
+        assert ei.value.status == sm.SM_ERR_MESH
+
+
+# ------------------------------------------- planner vs reference planner
+
+_CODE = {
+    "SPEC": sm.SM_ERR_SPEC, "AXIS_REUSED": sm.SM_ERR_AXIS_REUSED, "INDIVISIBLE": sm.SM_ERR_INDIVISIBLE,
+    "J_MISMATCH": sm.SM_ERR_J_MISMATCH, "SHAPE": sm.SM_ERR_SHAPE, "MESH": sm.SM_ERR_MESH,
+}
+
+
+def _all_specs(names):
+    """Every 2-D spec over the mesh axes with ordered axis lists (len <= 2 per dim)."""
+    lists = [()]
+    for k in (1, 2):
+        lists += list(itertools.permutations(names, k))
+    for d0 in lists:
+        for d1 in lists:
+            yield (tuple(d0), tuple(d1))
+
+
+def _to_c_spec(spec, names):
+    s = sm.sm_spec()
+    for d in range(2):
+        s.n[d] = len(spec[d])
+        for k, a in enumerate(spec[d]):
+            s.axes[d][k] = names.index(a)
+    return s
+
+
+def _compare(mesh_axes, a, b, I, J, K):
+    names = [n for n, _ in mesh_axes]
+    mesh = sm.sm_mesh_init(mesh_axes)
+    try:
+        want = ref_planner.plan(mesh_axes, a, b, I, J, K)
+        want_err = None
+    except ref_planner.PlanError as e:
+        want, want_err = None, e.code
+    try:
+        got = sm.sm_plan(mesh, _to_c_spec(a, names), _to_c_spec(b, names), I, J, K)
+        got_err = None
+    except sm.ShardmmError as e:
+        got, got_err = None, e.status
+    if want_err is not None:
+        assert got_err == _CODE[want_err], (mesh_axes, a, b)
+        return
+    assert got_err is None, (mesh_axes, a, b, got_err)
+    assert got.kase == want.case
+    assert got.n_ranks == want.n_ranks
+    assert tuple(got.a_local) == want.a_local and tuple(got.b_local) == want.b_local
+    assert tuple(got.c_local) == want.c_local
+    assert tuple(got.a_grid) == want.a_grid and tuple(got.b_grid) == want.b_grid
+    assert tuple(got.c_grid) == want.c_grid
+    assert (got.a_copies, got.b_copies, got.c_copies) == (want.a_copies, want.b_copies, want.c_copies)
+    assert got.n_partials == want.n_partials and got.n_groups == want.n_groups
+    red = tuple(names[i] for i in range(len(names)) if got.reduce_axes >> i & 1)
+    assert set(red) == set(want.unreduced)
+    if want.gather_operand is None:
+        assert got.gather_operand == -1
+    else:
+        assert got.gather_operand == "AB".index(want.gather_operand)
+        assert {names[i] for i in range(len(names)) if got.gather_axes >> i & 1} == set(want.gather_axes)
+    if want.case == 3:
+        assert tuple(tuple(names[i] for i in d) for d in got.c_rs.dims()) == want.c_rs_spec
+    for r in range(want.n_ranks):
+        ri = sm.sm_rank_info(got, r)
+        bl = want.rank_blocks(r)
+        assert tuple(ri.a_block) == bl["A"] and tuple(ri.b_block) == bl["B"] and tuple(ri.c_block) == bl["C"]
+        assert tuple(ri.coords[: len(names)]) == tuple(want.coords(r)[n] for n in names)
+        if want.case in (1, 3):
+            assert ri.unit == want.rank_unit(r)
+            if want.case == 3 and want.c_local[0] % want.n_partials == 0:
+                g, y = divmod(ri.unit, want.n_partials)
+                assert (ri.rs_row0, ri.rs_rows) == want.rs_rows(g, y)
+        else:
+            assert ri.unit == -1
+
+
+@pytest.mark.parametrize("mesh_axes", [
+    [("X", 2)], [("X", 3)], [("X", 1)], [("X", 4), ("Y", 2)], [("X", 2), ("Y", 3)],
+    [("X", 2), ("Y", 1), ("Z", 2)],
+])
+def test_planner_brute_force_against_reference(mesh_axes):
+    """Every legal and illegal 2-D spec pair on small meshes: the library's
+    planner and the oracle's planner agree on case, shapes, grids, copies,
+    reduce axes, gather choice, rank blocks, units and RS ownership."""
+    names = [n for n, _ in mesh_axes]
+    specs = list(_all_specs(names))
+    if len(names) == 3:
+        specs = [s for s in specs if len(s[0]) + len(s[1]) <= 2]
+    shapes = [(12, 12, 12), (24, 36, 12), (6, 5, 4)]
+    for a in specs:
+        for b in specs:
+            for I, J, K in shapes[:2] if len(names) < 3 else shapes[:1]:
+                _compare(mesh_axes, a, b, I, J, K)
+    _compare(mesh_axes, specs[1], specs[1], *shapes[2])
+
+
+def test_sandbox_default_through_the_library():
+    p = sm.sm_plan({"X": 4, "Y": 2}, "P('X', 'Y')", "P('Y', None)", 8192, 28672, 8192)
+    assert p.kase == sm.SM_CASE3 and tuple(p.a_local) == (2048, 14336) and p.a_copies == 1
+    assert tuple(p.a_grid) == (4, 2) and tuple(p.b_grid) == (2, 1) and p.n_ranks == 8
+    assert p.n_partials == 2 and p.n_groups == 4
+
+
+def test_plan_dtype_rules():
+    with pytest.raises(sm.ShardmmError) as ei:
+        sm.sm_plan({"X": 2}, "P(None, 'X')", "P('X', None)", 8, 8, 8, sm.SM_BF16, sm.SM_BF16)
+    assert ei.value.status == sm.SM_ERR_DTYPE  # partials must stay float32
+    with pytest.raises(sm.ShardmmError) as ei:
+        sm.sm_plan({"X": 2}, "P()", "P()", 8, 8, 8, sm.SM_F32, sm.SM_F32)
+    assert ei.value.status == sm.SM_ERR_DTYPE
+    p = sm.sm_plan({"X": 2}, "P()", "P(None, 'X')", 8, 8, 8, sm.SM_BF16, sm.SM_BF16)
+    assert p.kase == sm.SM_CASE1
+
+
+# ------------------------------------------------ host-side validation
+
+FAKE = 0x10000  # never dereferenced: every call below fails validation first
+
+
+def _fb(ld, stride=0, elems=1 << 40, ptr=FAKE):
+    return sm.sm_buf(ctypes.c_void_p(ptr), ld, stride, elems)
+
+
+def _err(fn, *args):
+    with pytest.raises(sm.ShardmmError) as ei:
+        fn(*args)
+    return ei.value.status
+
+
+def test_local_gemm_validation():
+    p3 = sm.sm_plan({"X": 2}, "P(None, 'X')", "P('X', None)", 64, 128, 64)
+    p2 = sm.sm_plan({"X": 2}, "P(None, 'X')", "P()", 64, 128, 64)
+    p4 = sm.sm_plan({"X": 2}, "P('X', None)", "P(None, 'X')", 64, 128, 64)
+    p1 = sm.sm_plan({"X": 2}, "P('X', None)", "P()", 64, 128, 64)
+    A, B = _fb(128), _fb(64)
+    Cs = _fb(64, 64 * 64)
+    assert _err(sm.sm_local_gemm, p2, A, B, Cs) == sm.SM_ERR_NEEDS_GATHER
+    assert _err(sm.sm_local_gemm, p4, A, B, Cs) == sm.SM_ERR_NEEDS_GATHER
+    assert _err(sm.sm_local_gemm, p3, A, B, _fb(64)) == sm.SM_ERR_UNREDUCED
+    assert _err(sm.sm_local_gemm, p3, A, B, Cs, sm.SM_EPI_GELU_TANH) == sm.SM_ERR_CASE
+    assert _err(sm.sm_local_gemm, p3, A, B, Cs, 7) == sm.SM_ERR_ARG
+    assert _err(sm.sm_local_gemm, p3, A, B, Cs, 0, 1, 2) == sm.SM_ERR_ARG
+    assert _err(sm.sm_local_gemm, p3, _fb(128, ptr=FAKE + 8), B, Cs) == sm.SM_ERR_ALIGN
+    assert _err(sm.sm_local_gemm, p3, _fb(130), B, Cs) == sm.SM_ERR_ALIGN
+    assert _err(sm.sm_local_gemm, p3, _fb(120), B, Cs) == sm.SM_ERR_SHAPE
+    assert _err(sm.sm_local_gemm, p3, _fb(128, elems=64 * 128 - 1), B, Cs) == sm.SM_ERR_SHAPE
+    assert _err(sm.sm_local_gemm, p3, A, B, _fb(64, 64 * 64, elems=2 * 64 * 64 - 1)) == sm.SM_ERR_SHAPE
+    assert _err(sm.sm_local_gemm, p3, A, B, _fb(64, 63 * 64)) == sm.SM_ERR_SHAPE
+    assert _err(sm.sm_local_gemm, p1, A, B, _fb(62)) == sm.SM_ERR_ALIGN
+    assert _err(sm.sm_local_gemm, p1, A, B, _fb(60)) == sm.SM_ERR_SHAPE
+    bad = sm.sm_plan_t()
+    assert _err(sm.sm_local_gemm, bad, A, B, Cs) == sm.SM_ERR_ARG
+
+
+def test_reduce_and_gather_validation():
+    p3 = sm.sm_plan({"X": 2, "Y": 2}, "P('X', 'Y')", "P('Y', None)", 12, 16, 8)
+    p1 = sm.sm_plan({"X": 2}, "P('X', None)", "P()", 8, 8, 8)
+    parts = _fb(8, 6 * 8)
+    out = _fb(8)
+    assert _err(sm.sm_reduce_partials, p1, parts, out) == sm.SM_ERR_CASE
+    assert _err(sm.sm_reduce_partials, p3, _fb(8), out) == sm.SM_ERR_UNREDUCED
+    assert _err(sm.sm_reduce_partials, p3, parts, out, 5) == sm.SM_ERR_ARG
+    assert _err(sm.sm_reduce_partials, p3, parts, out, sm.SM_ALLREDUCE, 1, 2) == sm.SM_ERR_ARG
+    assert _err(sm.sm_reduce_partials, p3, _fb(8, 6 * 8, elems=4 * 6 * 8 - 1), out) == sm.SM_ERR_SHAPE
+    q = sm.sm_plan({"X": 2, "Y": 4}, "P('X', 'Y')", "P('Y', None)", 12, 16, 8)  # m = 6, N = 4
+    assert _err(sm.sm_reduce_partials, q, parts, out, sm.SM_REDUCESCATTER) == sm.SM_ERR_INDIVISIBLE
+    assert _err(sm.sm_gather_shards, p3, sm.SM_WHAT_C_PARTIAL, parts, out) == sm.SM_ERR_UNREDUCED
+    assert _err(sm.sm_gather_shards, p1, sm.SM_WHAT_C_SCATTERED, _fb(8, 32), out) == sm.SM_ERR_CASE
+    assert _err(sm.sm_gather_shards, p1, sm.SM_WHAT_C_BLOCKS, _fb(8), out) == sm.SM_ERR_ARG
+    assert _err(sm.sm_gather_shards, p1, sm.SM_WHAT_C_BLOCKS, _fb(8, 32), _fb(8, 64)) == sm.SM_ERR_ARG
+    assert _err(sm.sm_gather_shards, p1, sm.SM_WHAT_C_BLOCKS, _fb(8, 32), _fb(4)) == sm.SM_ERR_SHAPE

@@ -1,0 +1,397 @@
+"""GPU parity: the HIP path, called through the C-ABI, against the fp64 oracle.
+
+Small and ragged shapes are checked element by element; the full workload
+sizes are checked in the launch configuration the benchmark times, on
+sampled output rows (float) or with exact Freivalds checks plus sampled
+entries (integers).
+"""
+import numpy as np
+import pytest
+import torch
+
+import local_shard_gemm_amd as sm
+import workloads as wl
+from oracle import planner, reference as ref
+
+from hip_cases import (DEV, REL_TOL, f32_bits_equal, guard_intact, guarded, run_partials, sample_rows, say,
+                       to_dev)
+
+pytestmark = pytest.mark.gpu
+
+
+def _plans(mesh, a_spec, b_spec, I, J, K, out=sm.SM_F32):
+    p = sm.sm_plan(mesh, a_spec, b_spec, I, J, K, sm.SM_BF16, out)
+    q = planner.plan(mesh, a_spec, b_spec, I, J, K, "bf16", "f32" if out == sm.SM_F32 else "bf16")
+    return p, q
+
+
+def _int(shape, seed):
+    return wl.random_ints(shape, seed)
+
+
+# --------------------------------------------------------------- toy (C0)
+
+def test_toy_case3_partials_allreduce_reducescatter_bitexact():
+    w = wl.get("toy")
+    say("case: toy", w.name)
+    A = wl.make_operand(w.operand("A"))
+    B = wl.make_operand(w.operand("B"))
+    p, q = _plans(dict(w.mesh), w.operand("A").spec, w.operand("B").spec, 64, 128, 64)
+    Ad, Bd = to_dev(A), to_dev(B)
+    full, P = run_partials(p, Ad, Bd)
+    parts = ref.partials(q, A, B)
+    torch.cuda.synchronize()
+    Pn = P.cpu().numpy()
+    for u in range(2):
+        assert f32_bits_equal(Pn[u], parts[u]), u
+    assert guard_intact(full, P.numel())
+    # all-reduce into the global layout
+    fo, out = guarded((64, 64), torch.float32)
+    sm.sm_reduce_partials(p, sm.buf(P), sm.buf(out), sm.SM_ALLREDUCE)
+    (s,) = ref.allreduce(q, parts)
+    assert f32_bits_equal(out.cpu().numpy(), s)
+    assert guard_intact(fo, out.numel())
+    # reduce-scatter: stacked row halves and global layout
+    frs, rs = guarded((2, 32, 64), torch.float32)
+    sm.sm_reduce_partials(p, sm.buf(P), sm.buf(rs), sm.SM_REDUCESCATTER)
+    want = ref.reduce_scatter(q, parts)
+    for y in range(2):
+        assert f32_bits_equal(rs[y].cpu().numpy(), want[(0, y)])
+    assert guard_intact(frs, rs.numel())
+    g = torch.empty(64, 64, dtype=torch.float32, device=DEV)
+    sm.sm_reduce_partials(p, sm.buf(P), sm.buf(g), sm.SM_REDUCESCATTER)
+    assert torch.equal(g, out)  # AR = RS + AG, bitwise
+    g2 = torch.empty(64, 64, dtype=torch.float32, device=DEV)
+    sm.sm_gather_shards(p, sm.SM_WHAT_C_SCATTERED, sm.buf(rs), sm.buf(g2))
+    assert torch.equal(g2, out)
+    # concatenation of partials is refused
+    with pytest.raises(sm.ShardmmError) as ei:
+        sm.sm_gather_shards(p, sm.SM_WHAT_C_PARTIAL, sm.buf(P), sm.buf(g2))
+    assert ei.value.status == sm.SM_ERR_UNREDUCED
+
+
+def test_two_by_two_worked_example():
+    """semiaifoundry.com 'Engineering example' on the GPU (ld = 8 buffers)."""
+    say("case: 2x2 worked example")
+    A = torch.zeros(2, 8, dtype=torch.bfloat16)
+    B = torch.zeros(2, 8, dtype=torch.bfloat16)
+    A[:, :2] = torch.tensor([[1, 2], [3, 4]], dtype=torch.bfloat16)
+    B[:, :2] = torch.tensor([[5, 6], [7, 8]], dtype=torch.bfloat16)
+    p = sm.sm_plan({"X": 2}, "P(None, 'X')", "P('X', None)", 2, 2, 2)
+    Ad, Bd = to_dev(A), to_dev(B)
+    P = torch.full((2, 2, 8), float("nan"), dtype=torch.float32, device=DEV)
+    sm.sm_local_gemm(p, sm.buf(Ad), sm.buf(Bd), sm.buf(P))
+    Pc = P.cpu()
+    assert Pc[0, :, :2].tolist() == [[5, 6], [15, 18]]
+    assert Pc[1, :, :2].tolist() == [[14, 16], [28, 32]]
+    assert torch.isnan(Pc[:, :, 2:]).all()  # nothing written outside the blocks
+    rs = torch.zeros(2, 1, 8, dtype=torch.float32, device=DEV)
+    sm.sm_reduce_partials(p, sm.buf(P), sm.buf(rs), sm.SM_REDUCESCATTER)
+    assert rs[0, 0, :2].tolist() == [19, 22] and rs[1, 0, :2].tolist() == [43, 50]
+    ar = torch.zeros(2, 8, dtype=torch.float32, device=DEV)
+    sm.sm_reduce_partials(p, sm.buf(P), sm.buf(ar), sm.SM_ALLREDUCE)
+    assert ar[:, :2].tolist() == [[19, 22], [43, 50]]
+
+
+# ------------------------------------------------ ragged edges (integers)
+
+RAGGED = [
+    # mesh, A spec, B spec, I, J, K
+    ({"X": 2, "Y": 2}, "P('X', 'Y')", "P('Y', None)", 600, 400, 520),   # K_local 200, N 520
+    ({"Y": 2}, "P(None, 'Y')", "P('Y', None)", 520, 256, 296),           # interior + edge tiles
+    ({"X": 3}, "P('X', None)", "P()", 3 * 257, 96, 264),                 # case 1, all ragged
+    ({"X": 2, "Y": 2}, "P('X', None)", "P(None, 'Y')", 2 * 512, 192, 2 * 256),  # case 1, interior only
+    ({"T": 4}, "P(None, 'T')", "P('T', None)", 300, 4 * 72, 256),         # K not a multiple of 64
+    ({"T": 2}, "P(None, 'T')", "P('T', None)", 33, 2 * 8, 17 * 8),        # tiny, one partial tile
+]
+
+
+@pytest.mark.parametrize("case", RAGGED, ids=lambda c: f"{c[3]}x{c[4]}x{c[5]}")
+def test_ragged_shapes_bitexact(case):
+    mesh, sa, sb, I, J, K = case
+    say("case: ragged", case)
+    A = _int((I, J), 11 + I)
+    B = _int((J, K), 12 + K)
+    p, q = _plans(mesh, sa, sb, I, J, K)
+    full, P = run_partials(p, to_dev(A), to_dev(B))
+    torch.cuda.synchronize()
+    Pn = P.cpu().numpy()
+    for u in range(q.n_units):
+        assert f32_bits_equal(Pn[u], ref.unit_partial(q, A, B, u)), u
+    assert guard_intact(full, P.numel())
+    if q.case == 3:
+        out = torch.empty(I, K, dtype=torch.float32, device=DEV)
+        sm.sm_reduce_partials(p, sm.buf(P), sm.buf(out), sm.SM_ALLREDUCE)
+        want = ref.gather(q, ref.allreduce(q, [ref.unit_partial(q, A, B, u) for u in range(q.n_units)]))
+        assert f32_bits_equal(out.cpu().numpy(), want)
+        np.testing.assert_array_equal(want, ref.dense(A, B))
+    else:
+        g = torch.empty(I, K, dtype=torch.float32, device=DEV)
+        sm.sm_gather_shards(p, sm.SM_WHAT_C_BLOCKS, sm.buf(P), sm.buf(g))
+        assert f32_bits_equal(g.cpu().numpy(), ref.dense(A, B))
+        # the global output layout of the local products gives the same bytes
+        g2 = torch.empty(I, K, dtype=torch.float32, device=DEV)
+        sm.sm_local_gemm(p, sm.buf(to_dev(A)), sm.buf(to_dev(B)), sm.buf(g2))
+        assert torch.equal(g, g2)
+
+
+SKINNY = [
+    ({"T": 4}, "P(None, 'T')", "P('T', None)", 5, 4 * 100, 296),    # ragged K and N
+    ({"T": 8}, "P(None, 'T')", "P('T', None)", 16, 8 * 256, 1024),  # full tiles
+    ({"T": 2}, "P(None, 'T')", "P('T', None)", 1, 2 * 64, 136),     # one row
+    ({"X": 2}, "P()", "P(None, 'X')", 16, 96, 2 * 128),              # case 1, skinny
+]
+
+
+@pytest.mark.parametrize("case", SKINNY, ids=lambda c: f"{c[3]}x{c[4]}x{c[5]}")
+def test_skinny_shapes_bitexact(case):
+    mesh, sa, sb, I, J, K = case
+    say("case: skinny", case)
+    A = _int((I, J), 21 + J)
+    B = _int((J, K), 22 + K)
+    p, q = _plans(mesh, sa, sb, I, J, K)
+    full, P = run_partials(p, to_dev(A), to_dev(B))
+    torch.cuda.synchronize()
+    Pn = P.cpu().numpy()
+    for u in range(q.n_units):
+        assert f32_bits_equal(Pn[u], ref.unit_partial(q, A, B, u)), u
+    assert guard_intact(full, P.numel())
+
+
+def test_gelu_epilogue_small():
+    """Case-1 column block with the GeLU(tanh) epilogue stored as bfloat16:
+    within one bfloat16 ulp of the oracle's round_bf16(gelu(.)), and the
+    second layer's reduced output within the float tolerance."""
+    say("case: gelu epilogue small")
+    X = wl.random_normal((96, 128), 31)
+    W1 = wl.random_normal((128, 4 * 160), 32, 0.1)
+    W2 = wl.random_normal((4 * 160, 128), 33, 0.1)
+    p1, q1 = _plans({"T": 4}, "P(None, None)", "P(None, 'T')", 96, 128, 640, sm.SM_BF16)
+    p2, q2 = _plans({"T": 4}, "P(None, 'T')", "P('T', None)", 96, 640, 128)
+    H = torch.empty(96, 640, dtype=torch.bfloat16, device=DEV)
+    sm.sm_local_gemm(p1, sm.buf(to_dev(X)), sm.buf(to_dev(W1)), sm.buf(H), sm.SM_EPI_GELU_TANH)
+    Hw, Zw = ref.mlp_chain(q1, q2, X, W1, W2)
+    Hg = H.cpu().view(torch.int16).numpy().view(np.uint16)
+    diff = np.abs(Hg.astype(np.int32) - Hw.astype(np.int32))
+    assert diff.max() <= 1 and (diff > 0).mean() < 0.01
+    P = torch.empty(4, 96, 128, dtype=torch.float32, device=DEV)
+    sm.sm_local_gemm(p2, sm.buf(H), sm.buf(to_dev(W2)), sm.buf(P))
+    Z = torch.empty(96, 128, dtype=torch.float32, device=DEV)
+    sm.sm_reduce_partials(p2, sm.buf(P), sm.buf(Z), sm.SM_ALLREDUCE)
+    assert ref.rel_frobenius(Z.cpu().numpy(), Zw) <= REL_TOL
+
+
+def test_determinism_and_stream_argument():
+    say("case: determinism")
+    A = wl.random_normal((512, 2 * 384), 41)
+    B = wl.random_normal((2 * 384, 512), 42)
+    p = sm.sm_plan({"Y": 2}, "P(None, 'Y')", "P('Y', None)", 512, 768, 512)
+    Ad, Bd = to_dev(A), to_dev(B)
+    s = torch.cuda.Stream()
+    outs = []
+    for _ in range(3):
+        P = torch.empty(2, 512, 512, dtype=torch.float32, device=DEV)
+        with torch.cuda.stream(s):
+            sm.sm_local_gemm(p, sm.buf(Ad), sm.buf(Bd), sm.buf(P), stream=s)
+            out = torch.empty(512, 512, dtype=torch.float32, device=DEV)
+            sm.sm_reduce_partials(p, sm.buf(P), sm.buf(out), sm.SM_ALLREDUCE, stream=s)
+        s.synchronize()
+        outs.append(out)
+    assert torch.equal(outs[0], outs[1]) and torch.equal(outs[1], outs[2])
+
+
+def test_unit_subsets_match_full_batch():
+    """Computing one X-group at a time equals the batched launch bitwise."""
+    say("case: unit subsets")
+    A = wl.random_normal((4 * 256, 2 * 256), 51)
+    B = wl.random_normal((2 * 256, 512), 52)
+    p = sm.sm_plan({"X": 4, "Y": 2}, "P('X', 'Y')", "P('Y', None)", 1024, 512, 512)
+    Ad, Bd = to_dev(A), to_dev(B)
+    _, P = run_partials(p, Ad, Bd)
+    for x in range(4):
+        _, Px = run_partials(p, Ad, Bd, 2 * x, 2)
+        assert torch.equal(Px, P[2 * x:2 * x + 2])
+
+
+# ------------------------------------------------- full workload sizes
+
+def _rel_err_rows(gpu_rows: np.ndarray, want_rows: np.ndarray) -> float:
+    return ref.rel_frobenius(gpu_rows, want_rows)
+
+
+@pytest.fixture(scope="module")
+def downproj():
+    w = wl.get("downproj")
+    A = wl.make_operand(w.operand("A"))
+    B = wl.make_operand(w.operand("B"))
+    return w, A, B
+
+
+def test_full_downproj_float(downproj):
+    """Case-3 down-projection shard at full size, all 8 units in one launch
+    and reduce-scatter of all 4 groups (the benchmarked configuration)."""
+    w, A, B = downproj
+    say("case: full downproj float")
+    I, J = A.shape
+    K = B.shape[1]
+    p, q = _plans(dict(w.mesh), w.operand("A").spec, w.operand("B").spec, I, J, K)
+    Ad, Bd = to_dev(A), to_dev(B)
+    full, P = run_partials(p, Ad, Bd)
+    rs = torch.empty(I, K, dtype=torch.float32, device=DEV)
+    sm.sm_reduce_partials(p, sm.buf(P), sm.buf(rs), sm.SM_REDUCESCATTER)
+    torch.cuda.synchronize()
+    assert guard_intact(full, P.numel())
+    m = q.c_local[0]
+    worst = 0.0
+    sums = {}
+    for u in range(q.n_units):
+        rows = sample_rows(m, 6, 100 + u)
+        want = ref.unit_partial(q, A, B, u, rows=rows)
+        got = P[u][rows].cpu().numpy()
+        worst = max(worst, _rel_err_rows(got, want))
+        g, y = divmod(u, q.n_partials)
+        sums.setdefault(g, []).append((rows, want))
+    say("downproj partial rel err", worst)
+    assert worst <= REL_TOL
+    # reduce-scatter rows: oracle partial rows summed in rank order
+    for g in range(q.n_groups):
+        rows = sample_rows(m, 4, 200 + g)
+        parts = [ref.unit_partial(q, A, B, g * q.n_partials + y, rows=rows) for y in range(q.n_partials)]
+        want = ref.sum_ranked(parts)
+        got = rs[[g * m + r for r in rows]].cpu().numpy()
+        assert _rel_err_rows(got, want) <= REL_TOL
+
+
+def test_full_downproj_integer_exact():
+    w = wl.int_variant(wl.get("downproj"))
+    say("case: full downproj integer")
+    A = wl.make_operand(w.operand("A"))
+    B = wl.make_operand(w.operand("B"))
+    I, J = A.shape
+    K = B.shape[1]
+    p, q = _plans(dict(w.mesh), w.operand("A").spec, w.operand("B").spec, I, J, K)
+    _, P = run_partials(p, to_dev(A), to_dev(B))
+    ar = torch.empty(4, *q.c_local, dtype=torch.float32, device=DEV)
+    sm.sm_reduce_partials(p, sm.buf(P), sm.buf(ar), sm.SM_ALLREDUCE)
+    rs = torch.empty(I, K, dtype=torch.float32, device=DEV)
+    sm.sm_reduce_partials(p, sm.buf(P), sm.buf(rs), sm.SM_REDUCESCATTER)
+    g = torch.empty(I, K, dtype=torch.float32, device=DEV)
+    sm.sm_gather_shards(p, sm.SM_WHAT_C_BLOCKS, sm.buf(ar), sm.buf(g))
+    assert torch.equal(g, rs)  # AR = RS + AG
+    Pn = P.cpu().numpy()
+    for u in range(q.n_units):
+        v = q.unit_views(u)
+        assert ref.freivalds(A, v["A"], B, v["B"], Pn[u].astype(np.float64), trials=1, seed=u) == 0.0, u
+        rng = np.random.default_rng(u)
+        ri = rng.integers(0, q.c_local[0], 256)
+        ci = rng.integers(0, q.c_local[1], 256)
+        want = ref.unit_entries(q, A, B, u, ri, ci)
+        assert np.array_equal(Pn[u][ri, ci], want.astype(np.float32))
+    # the reduced output against the dense product (exact), via Freivalds
+    assert ref.freivalds(A, (0, 0, I, J), B, (0, 0, J, K), rs.cpu().numpy().astype(np.float64), trials=1) == 0.0
+
+
+def test_full_case1_float_and_gather():
+    w = wl.get("case1")
+    say("case: full case1 float")
+    A = wl.make_operand(w.operand("A"))
+    B = wl.make_operand(w.operand("B"))
+    p, q = _plans(dict(w.mesh), w.operand("A").spec, w.operand("B").spec, 4096, 4096, 4096)
+    _, P = run_partials(p, to_dev(A), to_dev(B))
+    C = torch.empty(4096, 4096, dtype=torch.float32, device=DEV)
+    sm.sm_gather_shards(p, sm.SM_WHAT_C_BLOCKS, sm.buf(P), sm.buf(C))
+    torch.cuda.synchronize()
+    rows = sample_rows(4096, 24, 7)
+    want = ref.matmul(A, B, rows=rows)
+    assert _rel_err_rows(C[rows].cpu().numpy(), want) <= REL_TOL
+
+
+def test_full_case1_integer_exact():
+    w = wl.int_variant(wl.get("case1"))
+    say("case: full case1 integer")
+    A = wl.make_operand(w.operand("A"))
+    B = wl.make_operand(w.operand("B"))
+    p, q = _plans(dict(w.mesh), w.operand("A").spec, w.operand("B").spec, 4096, 4096, 4096)
+    _, P = run_partials(p, to_dev(A), to_dev(B))
+    C = torch.empty(4096, 4096, dtype=torch.float32, device=DEV)
+    sm.sm_gather_shards(p, sm.SM_WHAT_C_BLOCKS, sm.buf(P), sm.buf(C))
+    Cn = C.cpu().numpy().astype(np.float64)
+    assert ref.freivalds(A, (0, 0, 4096, 4096), B, (0, 0, 4096, 4096), Cn, trials=2) == 0.0
+    rows = sample_rows(4096, 8, 8)
+    assert f32_bits_equal(C[rows].cpu().numpy(), ref.matmul(A, B, rows=rows))
+
+
+def test_full_mlp_chain():
+    w = wl.get("mlp")
+    say("case: full mlp chain")
+    X = wl.make_operand(w.operand("X"))
+    W1 = wl.make_operand(w.operand("W1"))
+    W2 = wl.make_operand(w.operand("W2"))
+    p1, q1 = _plans(dict(w.mesh), w.operand("X").spec, w.operand("W1").spec, 4096, 4096, 16384, sm.SM_BF16)
+    p2, q2 = _plans(dict(w.mesh), "P(None, 'T')", w.operand("W2").spec, 4096, 16384, 4096)
+    H = torch.empty(4096, 16384, dtype=torch.bfloat16, device=DEV)  # column blocks, global layout
+    sm.sm_local_gemm(p1, sm.buf(to_dev(X)), sm.buf(to_dev(W1)), sm.buf(H), sm.SM_EPI_GELU_TANH)
+    P = torch.empty(4, 4096, 4096, dtype=torch.float32, device=DEV)
+    sm.sm_local_gemm(p2, sm.buf(H), sm.buf(to_dev(W2)), sm.buf(P))
+    Z = torch.empty(4096, 4096, dtype=torch.float32, device=DEV)
+    sm.sm_reduce_partials(p2, sm.buf(P), sm.buf(Z), sm.SM_ALLREDUCE)
+    torch.cuda.synchronize()
+    rows = sample_rows(4096, 8, 9)
+    Hw, Zw = ref.mlp_chain(q1, q2, X, W1, W2, rows=rows)
+    Hg = H[rows].cpu().view(torch.int16).numpy().view(np.uint16)
+    diff = np.abs(Hg.astype(np.int32) - Hw.astype(np.int32))
+    say("H ulp mismatches", int((diff > 0).sum()), "of", diff.size)
+    assert diff.max() <= 1 and (diff > 0).mean() < 0.01
+    err = _rel_err_rows(Z[rows].cpu().numpy(), Zw)
+    say("chain rel err", err)
+    assert err <= REL_TOL
+
+
+def test_full_mlp_integer_layers_exact():
+    """Both GEMM shapes of the chain with the plain store epilogue on
+    integer values (GeLU would break integrality)."""
+    w = wl.int_variant(wl.get("mlp"))
+    say("case: full mlp integer")
+    X = wl.make_operand(w.operand("X"))
+    W1 = wl.make_operand(w.operand("W1"))
+    W2 = wl.make_operand(w.operand("W2"))
+    p1, q1 = _plans(dict(w.mesh), w.operand("X").spec, w.operand("W1").spec, 4096, 4096, 16384)
+    _, P1 = run_partials(p1, to_dev(X), to_dev(W1))
+    for u in range(4):
+        v = q1.unit_views(u)
+        assert ref.freivalds(X, v["A"], W1, v["B"], P1[u].cpu().numpy().astype(np.float64), trials=1) == 0.0
+    H = wl.random_ints((4096, 16384), 4600)
+    p2, q2 = _plans(dict(w.mesh), "P(None, 'T')", w.operand("W2").spec, 4096, 16384, 4096)
+    _, P2 = run_partials(p2, to_dev(H), to_dev(W2))
+    Z = torch.empty(4096, 4096, dtype=torch.float32, device=DEV)
+    sm.sm_reduce_partials(p2, sm.buf(P2), sm.buf(Z), sm.SM_ALLREDUCE)
+    assert ref.freivalds(H, (0, 0, 4096, 16384), W2, (0, 0, 16384, 4096),
+                         Z.cpu().numpy().astype(np.float64), trials=1) == 0.0
+
+
+@pytest.mark.parametrize("integer", [False, True])
+def test_full_skinny_all_outputs(integer):
+    w = wl.get("skinny")
+    if integer:
+        w = wl.int_variant(w)
+    say("case: full skinny", "int" if integer else "float")
+    X = wl.make_operand(w.operand("X"))
+    A = wl.make_operand(w.operand("A"))
+    p, q = _plans(dict(w.mesh), w.operand("X").spec, w.operand("A").spec, 16, 28672, 8192)
+    full, P = run_partials(p, to_dev(X), to_dev(A))
+    out = torch.empty(16, 8192, dtype=torch.float32, device=DEV)
+    sm.sm_reduce_partials(p, sm.buf(P), sm.buf(out), sm.SM_ALLREDUCE)
+    torch.cuda.synchronize()
+    assert guard_intact(full, P.numel())
+    parts = ref.partials(q, X, A)
+    (s,) = ref.allreduce(q, parts)
+    Pn = P.cpu().numpy()
+    if integer:
+        for u in range(8):
+            assert f32_bits_equal(Pn[u], parts[u]), u
+        assert f32_bits_equal(out.cpu().numpy(), s)
+    else:
+        worst = max(ref.rel_frobenius(Pn[u], parts[u]) for u in range(8))
+        say("skinny partial rel err", worst)
+        assert worst <= REL_TOL
+        assert ref.rel_frobenius(out.cpu().numpy(), s) <= REL_TOL
