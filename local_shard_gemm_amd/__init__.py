@@ -217,7 +217,9 @@ def buf(t, ld: Optional[int] = None, block_stride: Optional[int] = None) -> sm_b
         ld = t.shape[-1]
     if block_stride is None:
         block_stride = t.shape[-2] * t.shape[-1] if t.dim() == 3 else 0
-    return sm_buf(ctypes.c_void_p(t.data_ptr()), int(ld), int(block_stride), int(t.numel()))
+    b = sm_buf(ctypes.c_void_p(t.data_ptr()), int(ld), int(block_stride), int(t.numel()))
+    b._tensor = t  # keep the memory alive as long as the descriptor
+    return b
 
 
 def _stream(stream):

@@ -77,10 +77,15 @@ __device__ __forceinline__ void transpose8(const uint4 (&in)[8], uint4 (&out)[8]
   }
 }
 
+// GeLU, tanh form: 0.5 x (1 + tanh(z)), z = sqrt(2/pi) (x + 0.044715 x^3),
+// evaluated as x / (1 + exp(-2 z)) -- the same function (1 + tanh(z) =
+// 2 / (1 + exp(-2z))) without the float32 cancellation of 1 + tanh(z) for
+// negative z.
 __device__ __forceinline__ float gelu_tanh_f32(float x) {
   const float k0 = 0.7978845608028654f;  // sqrt(2/pi)
   const float k1 = 0.044715f;
-  return 0.5f * x * (1.0f + tanhf(k0 * (x + k1 * x * x * x)));
+  const float z = k0 * (x + k1 * x * x * x);
+  return x / (1.0f + expf(-2.0f * z));
 }
 
 // float -> bfloat16, round to nearest even (NaN stays NaN).

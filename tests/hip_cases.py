@@ -64,6 +64,28 @@ def run_partials(plan, A_dev, B_dev, unit_begin=0, unit_count=None, stream=None)
     return full, C
 
 
+def bf16_ulp(v: np.ndarray) -> np.ndarray:
+    """Spacing of bfloat16 numbers at |v| (8 significant bits)."""
+    a = np.abs(np.asarray(v, dtype=np.float64))
+    _, ex = np.frexp(a)
+    return np.where(a > 0, np.ldexp(1.0, np.maximum(ex - 8, -133)), 2.0 ** -133)
+
+
+def gelu_h_within_bound(h_gpu_bits, h_oracle_bits, abs_dot: np.ndarray, k: int) -> np.ndarray:
+    """Elementwise check of bfloat16 GeLU outputs against the oracle.
+
+    The GPU's float32 pre-activation differs from the exact one by at most
+    k * 2^-24 * sum_j |x_j w_j| (a standard bound for recursive float32
+    summation of k products, each exact); GeLU(tanh) has slope at most 1.13,
+    and each side rounds once to bfloat16. So
+      |H_gpu - H_oracle| <= 1.13 * k * 2^-24 * sum|x w| + ulp(max |H|).
+    """
+    hg = ref.bf16_bits_to_f64(np.asarray(h_gpu_bits))
+    hw = ref.bf16_bits_to_f64(np.asarray(h_oracle_bits))
+    bound = 1.13 * k * 2.0 ** -24 * abs_dot + bf16_ulp(np.maximum(np.abs(hg), np.abs(hw)))
+    return np.abs(hg - hw) <= bound
+
+
 def sample_rows(m: int, k: int, seed: int):
     rng = np.random.default_rng(seed)
     rows = set(rng.choice(m, size=min(k, m), replace=False).tolist())
