@@ -236,11 +236,255 @@ __device__ __forceinline__ void run_tile(const GemmLaunch& L, const uint16_t* __
   store_tile<OUT_BF16, GELU, EDGE>(acc, C, L.ldc, row0, col0, M, N);
 }
 
-// Interior tiles: every tile of the launch is a full BM x BN tile and K is a
-// multiple of BK, so no load or store needs a bounds check.
+// ---------------------------------------------------------------------------
+// Interior tiles: direct HBM -> LDS pipeline.
+//
+//  * Both operands travel global -> LDS with global_load_lds_dwordx4 (16
+//    bytes per lane, landing at M0 + 16 * lane): no staging registers, no
+//    LDS stores, no register transpose.
+//  * K advances 32 at a time through 4 LDS stages of 32 KiB (A 256x32, B
+//    32x256); loads run 3 stages ahead of the matrix cores.
+//  * A stage: row r holds 32 k (64 bytes = 4 chunks); chunk c of row r sits
+//    at c ^ ((r >> 2) & 3). A fragments are 16-byte LDS reads (8 k of one
+//    row per lane).
+//  * B stage: row k holds 256 n (512 bytes = 32 chunks); chunk c of row k
+//    sits at c ^ ((k & 3) << 2). B stays N-contiguous in LDS; the MFMA's
+//    k-packed fragment is read with ds_read_b64_tr_b16, which (per 16-lane
+//    group) takes lane 4r+q's 4 consecutive elements as row r, columns
+//    4q..4q+3 of a 4x16 tile and returns column j to lane j. Two such reads
+//    give a lane the 8 k values of its column.
+//  * Both swizzles make every fragment read touch each LDS bank the minimum
+//    number of times.
+//  * Fragments for the next 16-k step are read while the current step's 16
+//    MFMAs run; the first step of a stage overlaps the previous stage's last
+//    MFMAs (issued after the barrier).
+// ---------------------------------------------------------------------------
+constexpr int BK2 = 32;
+constexpr int STAGES = 4;
+constexpr int A_STAGE = BM * BK2 * 2;  // bytes
+constexpr int B_STAGE = BK2 * BN * 2;
+constexpr int STAGE_BYTES = A_STAGE + B_STAGE;
+
+typedef __attribute__((address_space(3))) char lds_char;
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) uint4 lds_u4;
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+// s_waitcnt with only vmcnt = n (expcnt and lgkmcnt left unconstrained).
+template <int n>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(n >= 0 && n < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((n & 0xF) | ((n >> 4) << 14) | 0x70 | 0xF00);
+}
+
+// s_waitcnt lgkmcnt(0) only (vmcnt left at its maximum, 63).
+__device__ __forceinline__ void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(0xF | (3 << 14) | 0x70); }
+
+struct Frags {
+  bf16x8 a[4];
+  bf16x8 b[4];
+};
+
+template <bool OUT_BF16, bool GELU>
+__device__ __forceinline__ void run_tile_lds(const GemmLaunch& L, const uint16_t* __restrict__ A,
+                                             const uint16_t* __restrict__ B, void* C, int row0, int col0,
+                                             lds_char* smem) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int64_t lda = L.lda, ldb = L.ldb;
+
+  // ---- loader: each wave fills 4 KiB of A and 4 KiB of B per stage, 1 KiB
+  // per instruction. A: rows (4w+i)*16 + lane/4, physical chunk lane%4;
+  // B: rows (4w+i)*2 + lane/32, physical chunk lane%32.
+  const uint16_t* ga[4];
+  const uint16_t* gb[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int ra = (4 * wave + i) * 16 + (lane >> 2);
+    const int ca = (lane & 3) ^ ((ra >> 2) & 3);
+    ga[i] = A + static_cast<int64_t>(row0 + ra) * lda + 8 * ca;
+    const int rb = (4 * wave + i) * 2 + (lane >> 5);
+    const int cb = (lane & 31) ^ ((rb & 3) << 2);
+    gb[i] = B + static_cast<int64_t>(rb) * ldb + col0 + 8 * cb;
+  }
+  auto issue = [&](int kt) {
+    lds_char* st = smem + (kt % STAGES) * STAGE_BYTES;
+    const int64_t ka = static_cast<int64_t>(kt) * BK2;
+    const int64_t kb = ka * ldb;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      __builtin_amdgcn_global_load_lds(ga[i] + ka, (lds_void*)(st + (4 * wave + i) * 1024), 16, 0, 0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      __builtin_amdgcn_global_load_lds(gb[i] + kb, (lds_void*)(st + A_STAGE + (4 * wave + i) * 1024), 16, 0, 0);
+  };
+
+  // ---- fragment addresses (byte offsets inside a stage)
+  int a_off[2][4];
+  int b_off[2][4][2];
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi) {
+      const int r = wm * 128 + mi * 32 + (lane & 31);
+      const int c = 2 * s + (lane >> 5);
+      a_off[s][mi] = r * (BK2 * 2) + ((c ^ ((r >> 2) & 3)) << 4);
+    }
+    const int g = lane >> 4, j = lane & 15, rr = j >> 2, q = j & 3, h = lane >> 5;
+#pragma unroll
+    for (int ni = 0; ni < 4; ++ni)
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const int kr = 16 * s + 8 * h + 4 * t + rr;
+        const int col = wn * 128 + ni * 32 + 16 * (g & 1) + 4 * q;
+        const int ch = col >> 3, half = (col >> 2) & 1;
+        b_off[s][ni][t] = A_STAGE + kr * (BN * 2) + ((ch ^ ((kr & 3) << 2)) << 4) + half * 8;
+      }
+  }
+  auto read_frags = [&](Frags& F, int kt, int s) {
+    lds_char* st = smem + (kt % STAGES) * STAGE_BYTES;
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi)
+      F.a[mi] = __builtin_bit_cast(bf16x8, *(lds_u4*)(st + a_off[s][mi]));
+#pragma unroll
+    for (int ni = 0; ni < 4; ++ni) {
+      const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(st + b_off[s][ni][0]));
+      const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(st + b_off[s][ni][1]));
+      F.b[ni] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    }
+  };
+
+  f32x16 acc[4][4];
+#pragma unroll
+  for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < 4; ++ni)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[mi][ni][v] = 0.0f;
+  auto mma = [&](const Frags& F) {
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < 4; ++ni)
+        acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(F.a[mi], F.b[ni], acc[mi][ni], 0, 0, 0);
+  };
+
+  const int nk = L.K / BK2;
+  // prologue: stages 0..2 in flight
+#pragma unroll
+  for (int p = 0; p < STAGES - 1; ++p)
+    if (p < nk) issue(p);
+
+  // F1 starts as zeros so that every iteration has the same straight-line
+  // body (its first MFMA step adds exact zeros).
+  Frags F0, F1;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    F1.a[i] = bf16x8{};
+    F1.b[i] = bf16x8{};
+  }
+  // Own LDS reads finished (the buffer refilled next was read last step),
+  // then a bare barrier: a full __syncthreads() fence would also wait for
+  // the loads still in flight for later stages.
+  auto stage_barrier = [&]() {
+    wait_lgkmcnt0();
+    asm volatile("" ::: "memory");  // keep LDS reads and DMA issues on their side
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
+
+  // Steady state: the body is one straight-line block so the scheduler can
+  // interleave. Per stage and wave: 8 DMA loads (stage kt+3), 24 fragment
+  // reads and 32 MFMAs. Each half: 12 fragment reads in the shadow of the
+  // first 6 MFMAs, 4 DMA loads in the shadow of the next 4, then 6 MFMAs;
+  // spreading the DMA keeps the 4 waves from queueing on the address unit
+  // right after the barrier.
+  // One fragment-read item (0..11): A fragments 0..3, then the two
+  // transposing halves of B fragments 0..3.
+  auto read_item = [&](Frags& F, lds_char* st, int s, int item) {
+    if (item < 4) {
+      F.a[item] = __builtin_bit_cast(bf16x8, *(lds_u4*)(st + a_off[s][item]));
+    } else {
+      const int ni = (item - 4) >> 1, t = (item - 4) & 1;
+      const bf16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(st + b_off[s][ni][t]));
+      if (t == 0)
+        F.b[ni] = __builtin_shufflevector(v, F.b[ni].hi, 0, 1, 2, 3, 4, 5, 6, 7);
+      else
+        F.b[ni] = __builtin_shufflevector(F.b[ni].lo, v, 0, 1, 2, 3, 4, 5, 6, 7);
+    }
+  };
+  // One DMA item (0..7): A rows for 0..3, B rows for 4..7.
+  auto dma_item = [&](int kt_load, int item) {
+    lds_char* st = smem + (kt_load % STAGES) * STAGE_BYTES;
+    const int64_t ka = static_cast<int64_t>(kt_load) * BK2;
+    if (item < 4)
+      __builtin_amdgcn_global_load_lds(ga[item] + ka, (lds_void*)(st + (4 * wave + item) * 1024), 16, 0, 0);
+    else
+      __builtin_amdgcn_global_load_lds(gb[item - 4] + ka * ldb,
+                                       (lds_void*)(st + A_STAGE + (4 * wave + item - 4) * 1024), 16, 0, 0);
+  };
+  // Half a stage in fixed program order: 16 MFMAs on `cur`; the 12
+  // fragment reads of `nxt` ride on the first 6, and DMA items
+  // [dma0, dma0+4) (if any) on the next 4. sched_barrier(0) pins the order.
+  auto half = [&](const Frags& cur, Frags& nxt, lds_char* st_next, int s_next, int kt_load, int dma0) {
+#pragma unroll
+    for (int idx = 0; idx < 16; ++idx) {
+      const int mi = idx >> 2, ni = idx & 3;
+      acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur.a[mi], cur.b[ni], acc[mi][ni], 0, 0, 0);
+      if (idx < 6) {
+        read_item(nxt, st_next, s_next, 2 * idx);
+        read_item(nxt, st_next, s_next, 2 * idx + 1);
+      } else if (idx < 10 && dma0 >= 0) {
+        dma_item(kt_load, dma0 + idx - 6);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  int kt = 0;
+  for (; kt + STAGES - 1 < nk; ++kt) {
+    wait_vmcnt<16>();  // this wave's loads of stage kt have landed
+    stage_barrier();   // ... and every wave's; buffer of stage kt-1 is free
+    lds_char* st = smem + (kt % STAGES) * STAGE_BYTES;
+    half(F1, F0, st, 0, kt + STAGES - 1, 0);  // previous stage's last step; A loads of stage kt+3
+    half(F0, F1, st, 1, kt + STAGES - 1, 4);  // B loads of stage kt+3
+  }
+  // Last stages: nothing left to load.
+  for (; kt < nk; ++kt) {
+    if (kt + 2 < nk)
+      wait_vmcnt<16>();
+    else if (kt + 1 < nk)
+      wait_vmcnt<8>();
+    else
+      wait_vmcnt<0>();
+    stage_barrier();
+    read_frags(F0, kt, 0);
+    mma(F1);
+    read_frags(F1, kt, 1);
+    mma(F0);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+#pragma unroll
+      for (int i = 0; i < 6; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 10, 0);
+    }
+  }
+  mma(F1);
+
+  store_tile<OUT_BF16, GELU, false>(acc, C, L.ldc, row0, col0, L.M, L.N);
+}
+
+// Interior tiles: every tile of the launch is a full BM x BN tile, K is a
+// multiple of 32 and every view is 16-byte aligned, so no load or store
+// needs a bounds check.
 template <bool OUT_BF16, bool GELU>
 __global__ __launch_bounds__(NT, 1) void gemm_bf16_mfma_kernel(const GemmLaunch L) {
-  __shared__ uint4 lds[2 * 2 * BM * CH];
+  __shared__ __attribute__((aligned(1024))) char smem[STAGES * STAGE_BYTES];
   const int full_m = L.M / BM, full_n = L.N / BN;
   const int VR = L.n_units * full_m;
   const int T = VR * full_n;
@@ -250,19 +494,24 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16_mfma_kernel(const GemmLaunch 
   const int row0 = (vr - unit * full_m) * BM;
   const int col0 = vc * BN;
   const GemmUnitPtrs U = L.u[unit];
-  run_tile<false, OUT_BF16, GELU>(L, U.a, U.b, U.c, row0, col0, lds);
+  run_tile_lds<OUT_BF16, GELU>(L, U.a, U.b, U.c, row0, col0, (lds_char*)smem);
+}
+
+// Every tile goes to the edge kernel when K is not a multiple of 32 or a
+// view is not 16-byte aligned.
+__host__ __device__ __forceinline__ bool all_tiles_edge(const GemmLaunch& L) {
+  return (L.K % BK2) != 0 || !L.vec_ok;
 }
 
 // Edge tiles: the last tile row (M % BM), the last tile column (N % BN), or
-// every tile when K % BK != 0 or a view is not 16-byte aligned. Loads
-// outside the views read as zero and stores outside them are skipped.
-// blockIdx.y = unit.
+// every tile (all_tiles_edge). Loads outside the views read as zero and
+// stores outside them are skipped. blockIdx.y = unit.
 template <bool OUT_BF16, bool GELU>
 __global__ __launch_bounds__(NT, 1) void gemm_bf16_mfma_edge_kernel(const GemmLaunch L) {
   __shared__ uint4 lds[2 * 2 * BM * CH];
   const int unit = blockIdx.y;
   int tm, tn;
-  if ((L.K % BK) || !L.vec_ok) {
+  if (all_tiles_edge(L)) {
     tm = blockIdx.x / L.tiles_n;
     tn = blockIdx.x % L.tiles_n;
   } else {
@@ -283,7 +532,7 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16_mfma_edge_kernel(const GemmLa
 template <bool OUT_BF16, bool GELU>
 hipError_t launch_variant(const GemmLaunch& L, hipStream_t s) {
   const int full_m = L.M / BM, full_n = L.N / BN;
-  const bool k_ragged = (L.K % BK) != 0 || !L.vec_ok;
+  const bool k_ragged = all_tiles_edge(L);
   if (!k_ragged && full_m > 0 && full_n > 0) {
     const int T = L.n_units * full_m * full_n;
     hipLaunchKernelGGL((gemm_bf16_mfma_kernel<OUT_BF16, GELU>), dim3(T), dim3(NT), 0, s, L);
