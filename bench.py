@@ -164,6 +164,13 @@ def main() -> int:
     red_bytes = (N + 1) * m * n * 4.0 * p.n_groups if p.kase == sm.SM_CASE3 else 0.0
     gemm_tflops = gemm_flops / (gemm_avg * 1e-3) / 1e12
     red_gbps = red_bytes / (red_avg * 1e-3) / 1e9 if red_bytes else 0.0
+    # algorithmic HBM bytes of the local products: each distinct operand
+    # block read once, each output written once
+    a_bytes = 2.0 * ctx["I"] * ctx["J"]
+    b_bytes = 2.0 * ctx["J"] * ctx["K"]
+    gemm_bytes = a_bytes + b_bytes + 4.0 * m * n * p.n_units
+    gemm_gbps = gemm_bytes / (gemm_avg * 1e-3) / 1e9
+    skinny = m <= 16
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -193,11 +200,14 @@ def main() -> int:
                       + f" {p.n_groups} groups x {N} fp32 partials [{m},{n}]",
         },
         "gemm": {"avg_ms": round(gemm_avg, 4), "min_ms": round(gemm_ms[0], 4),
-                 "tflops": round(gemm_tflops, 1), "frac_of_peak": round(gemm_tflops / PEAK_BF16_TFLOPS, 4)},
+                 "tflops": round(gemm_tflops, 1), "frac_of_peak": round(gemm_tflops / PEAK_BF16_TFLOPS, 4),
+                 "bytes": gemm_bytes, "gbps": round(gemm_gbps, 1)},
         "reduce": {"avg_ms": round(red_avg, 4), "min_ms": round(red_ms[0], 4), "bytes": red_bytes,
                    "gbps": round(red_gbps, 1), "frac_of_peak": round(red_gbps / PEAK_HBM_GBPS, 4)},
-        "roofline": {"bound": "mfma", "achieved": round(gemm_tflops, 1), "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(gemm_tflops / PEAK_BF16_TFLOPS, 4), "traffic": None},
+        "roofline": ({"bound": "hbm", "achieved": round(gemm_gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                      "frac": round(gemm_gbps / PEAK_HBM_GBPS, 4), "traffic": None} if skinny else
+                     {"bound": "mfma", "achieved": round(gemm_tflops, 1), "peak": PEAK_BF16_TFLOPS,
+                      "unit": "TFLOP/s", "frac": round(gemm_tflops / PEAK_BF16_TFLOPS, 4), "traffic": None}),
         "roofline_reduce": {"bound": "hbm", "achieved": round(red_gbps, 1), "peak": PEAK_HBM_GBPS,
                             "unit": "GB/s", "frac": round(red_gbps / PEAK_HBM_GBPS, 4), "traffic": None},
         "cpu_baseline": cpu,

@@ -4,14 +4,18 @@
 // The local matmul each rank runs after sharding (learntpu.dev ch05,
 // sharding sandbox "Local matmul"; lingze.zone "Case 1" and "Case 3").
 //
-// Design (gfx950, wave64):
-//  * 256x256 output tile per workgroup of 4 waves (2x2); each wave owns a
-//    128x128 sub-tile = 4x4 MFMA blocks of v_mfma_f32_32x32x16_bf16, i.e.
-//    256 fp32 accumulators per lane.
+// Two kernels share the 256x256 output tile per workgroup of 4 waves (2x2),
+// each wave owning a 128x128 sub-tile = 4x4 MFMA blocks of
+// v_mfma_f32_32x32x16_bf16 (256 fp32 accumulators per lane):
+//  * gemm_bf16_mfma_kernel (interior tiles): direct HBM -> LDS loads and
+//    transposing LDS reads, a 4-stage pipeline; described above run_tile_lds.
+//  * gemm_bf16_mfma_edge_kernel (ragged M/N/K, unaligned views): guarded
+//    loads through registers, described here.
+//
+// Edge-tile design:
 //  * K advances 64 at a time through two LDS buffers (2 x 64 KiB): the
-//    next slice is fetched from HBM into registers while the current one
-//    feeds the matrix cores, then written to the other buffer; one barrier
-//    per slice.
+//    next slice is fetched into registers while the current one feeds the
+//    matrix cores, then written to the other buffer; one barrier per slice.
 //  * A is row-major [M,K] (K contiguous): 16-byte chunks go to LDS as is.
 //    B is row-major [K,N] (N contiguous) but the MFMA wants 8 consecutive
 //    k per lane: each thread loads an 8(k) x 8(n) block and transposes it
@@ -20,6 +24,8 @@
 //    at c ^ ((r ^ r>>3) & 7), which keeps both the row-wise stores and the
 //    MFMA fragment reads (8 consecutive rows, same chunk) free of bank
 //    conflicts.
+//
+// Both kernels:
 //  * Tile order: groups of 16 tile rows, column-major inside a group, and
 //    inside every full chunk of 256 workgroups an XCD-aware permutation
 //    that gives each of the 8 XCDs (workgroup id mod 8) a 4x8 block of
@@ -427,7 +433,9 @@ __device__ __forceinline__ void run_tile_lds(const GemmLaunch& L, const uint16_t
   };
   // Half a stage in fixed program order: 16 MFMAs on `cur`; the 12
   // fragment reads of `nxt` ride on the first 6, and DMA items
-  // [dma0, dma0+4) (if any) on the next 4. sched_barrier(0) pins the order.
+  // [dma0, dma0+4) (if any) on MFMAs 3, 7, 11 and 15 -- one DMA per four
+  // MFMAs per wave keeps the address unit below saturation with 4 waves.
+  // sched_barrier(0) pins the order.
   auto half = [&](const Frags& cur, Frags& nxt, lds_char* st_next, int s_next, int kt_load, int dma0) {
 #pragma unroll
     for (int idx = 0; idx < 16; ++idx) {
@@ -436,9 +444,8 @@ __device__ __forceinline__ void run_tile_lds(const GemmLaunch& L, const uint16_t
       if (idx < 6) {
         read_item(nxt, st_next, s_next, 2 * idx);
         read_item(nxt, st_next, s_next, 2 * idx + 1);
-      } else if (idx < 10 && dma0 >= 0) {
-        dma_item(kt_load, dma0 + idx - 6);
       }
+      if ((idx & 3) == 3 && dma0 >= 0) dma_item(kt_load, dma0 + (idx >> 2));
       __builtin_amdgcn_sched_barrier(0);
     }
   };
