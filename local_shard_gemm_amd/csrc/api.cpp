@@ -184,10 +184,23 @@ int32_t run_jobs(std::vector<RowJob>& jobs, int32_t n_sum, int32_t elem_bytes, h
     L.n_sum = n_sum;
     L.elem_bytes = elem_bytes;
     L.max_rows = 0;
+    int32_t max_cols = 0;
     for (size_t i = 0; i < cnt; ++i) {
       L.jobs[i] = jobs[first + i];
       L.max_rows = std::max(L.max_rows, L.jobs[i].rows);
+      max_cols = std::max(max_cols, L.jobs[i].cols);
     }
+    // Few rows: split rows into column chunks (>= 1024 columns each) so that
+    // the launch has enough workgroups to keep HBM busy.
+    const int64_t base = static_cast<int64_t>(cnt) * L.max_rows;
+    int64_t n_chunks = 1;
+    if (base < 2048) n_chunks = std::min<int64_t>((2048 + base - 1) / base, (max_cols + 1023) / 1024);
+    n_chunks = std::max<int64_t>(n_chunks, 1);
+    int64_t chunk = (max_cols + n_chunks - 1) / n_chunks;
+    chunk = (chunk + 7) / 8 * 8;
+    L.chunk = static_cast<int32_t>(chunk);
+    L.n_chunks = static_cast<int32_t>((max_cols + chunk - 1) / chunk);
+    if (static_cast<int64_t>(L.max_rows) * L.n_chunks > INT32_MAX) return fail(SM_ERR_SHAPE, "too many rows");
     hipError_t e = launch_rows(L, s);
     if (e != hipSuccess) return hip_fail(e, where);
   }

@@ -8,8 +8,9 @@
 //    ranks on one GPU the "collective" is this HBM-bound pass.
 //  * Copy (n_sum = 1): all-gather of finished blocks into the global layout.
 //
-// Design (gfx950): pure streaming. Each workgroup owns one row of one job;
-// its 256 threads walk the row in 16-byte vectors, four vectors per thread
+// Design (gfx950): pure streaming. Each workgroup owns one row (or one
+// column chunk of a row, when a launch has few rows) of one job; its 256
+// threads walk it in 16-byte vectors, four vectors per thread
 // per iteration, and issue every partial's loads before the rank-ordered
 // adds so that 4 x N loads per thread are in flight. Loads and stores are
 // non-temporal: nothing is re-read, so the data should not displace L2.
@@ -117,11 +118,25 @@ __device__ __forceinline__ void copy_row_16_scalar(const RowJob& J, int row) {
   for (int c = threadIdx.x; c < J.cols; c += NT) dst[c] = src[c];
 }
 
+// Workgroup -> (job, row, column chunk). Jobs with few rows are split into
+// column chunks so that small reductions still spread over many CUs.
+__device__ __forceinline__ bool job_slice(const RowLaunch& L, RowJob& J, int& row) {
+  J = L.jobs[blockIdx.y];
+  row = blockIdx.x / L.n_chunks;
+  const int c0 = (blockIdx.x - row * L.n_chunks) * L.chunk;
+  if (row >= J.rows || c0 >= J.cols) return false;
+  const int64_t off = static_cast<int64_t>(c0) * L.elem_bytes;
+  J.src = static_cast<const char*>(J.src) + off;
+  J.dst = static_cast<char*>(J.dst) + off;
+  J.cols = min(J.cols - c0, L.chunk);
+  return true;
+}
+
 template <int NS>
 __global__ __launch_bounds__(NT) void rows_f32_kernel(const RowLaunch L) {
-  const RowJob& J = L.jobs[blockIdx.y];
-  const int row = blockIdx.x;
-  if (row >= J.rows) return;
+  RowJob J;
+  int row;
+  if (!job_slice(L, J, row)) return;
   if (J.vec)
     sum_row_vec<NS>(J, L.n_sum, row);
   else
@@ -129,9 +144,9 @@ __global__ __launch_bounds__(NT) void rows_f32_kernel(const RowLaunch L) {
 }
 
 __global__ __launch_bounds__(NT) void rows_b16_copy_kernel(const RowLaunch L) {
-  const RowJob& J = L.jobs[blockIdx.y];
-  const int row = blockIdx.x;
-  if (row >= J.rows) return;
+  RowJob J;
+  int row;
+  if (!job_slice(L, J, row)) return;
   if (J.vec)
     copy_row_16(J, row);
   else
@@ -141,8 +156,8 @@ __global__ __launch_bounds__(NT) void rows_b16_copy_kernel(const RowLaunch L) {
 }  // namespace
 
 hipError_t launch_rows(const RowLaunch& L, hipStream_t s) {
-  if (L.n_jobs <= 0 || L.max_rows <= 0) return hipSuccess;
-  dim3 grid(L.max_rows, L.n_jobs);
+  if (L.n_jobs <= 0 || L.max_rows <= 0 || L.n_chunks <= 0) return hipSuccess;
+  dim3 grid(L.max_rows * L.n_chunks, L.n_jobs);
   if (L.elem_bytes == 2) {
     hipLaunchKernelGGL(rows_b16_copy_kernel, grid, dim3(NT), 0, s, L);
   } else {
