@@ -172,6 +172,25 @@ def main() -> int:
     gemm_gbps = gemm_bytes / (gemm_avg * 1e-3) / 1e9
     skinny = m <= 16
 
+    # The fused kernel (local products and rank-ordered reduction in one
+    # launch, no partial buffers) on the same inputs, timed the same way.
+    fused = None
+    if p.kase == sm.SM_CASE3 and m > 16:
+        fev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+        for _ in range(2):
+            sm.sm_local_gemm_reduce(p, a, b, o, mode, 0, p.n_groups, stream)
+        torch.cuda.synchronize()
+        for k in range(args.steps):
+            fev[k][0].record(stream)
+            sm.sm_local_gemm_reduce(p, a, b, o, mode, 0, p.n_groups, stream)
+            fev[k][1].record(stream)
+        torch.cuda.synchronize()
+        f_ms = sorted(e[0].elapsed_time(e[1]) for e in fev)
+        f_avg = sum(f_ms) / len(f_ms)
+        fused = {"avg_ms": round(f_avg, 4), "min_ms": round(f_ms[0], 4),
+                 "tflops": round(gemm_flops / (f_avg * 1e-3) / 1e12, 1),
+                 "vs_gemm_plus_reduce": round((gemm_avg + red_avg) / f_avg, 3)}
+
     cpu = None
     if not args.no_cpu_baseline:
         log(f"bench: oracle CPU baseline on {args.cpu_rows} rows")
@@ -210,6 +229,7 @@ def main() -> int:
                       "unit": "TFLOP/s", "frac": round(gemm_tflops / PEAK_BF16_TFLOPS, 4), "traffic": None}),
         "roofline_reduce": {"bound": "hbm", "achieved": round(red_gbps, 1), "peak": PEAK_HBM_GBPS,
                             "unit": "GB/s", "frac": round(red_gbps / PEAK_HBM_GBPS, 4), "traffic": None},
+        "fused_gemm_reduce": fused,
         "cpu_baseline": cpu,
         "context": "learntpu.dev sandbox, modelled (not measured) on Ironwood: 481 GFLOP local matmul "
                    "in 209 us per rank",

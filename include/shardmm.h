@@ -177,6 +177,17 @@ int32_t sm_plan(const sm_mesh* mesh, const sm_spec* a, const sm_spec* b,
 /* Where rank `rank` sits in the plan. */
 int32_t sm_rank_info(const sm_plan_t* plan, int32_t rank, sm_rank_info_t* out);
 
+/* Cases 2 and 4 by composition (lingze.zone "Case 2" and "Case 4": all-gather
+ * the offending operand, then multiply locally; learntpu.dev ch05, the four
+ * cases). Given a case-2 or case-4 plan, fill *out with the plan that holds
+ * after plan->gather_operand has been all-gathered over plan->gather_axes
+ * (those axes removed from that operand's spec): case 1 or 3, or case 2
+ * when a case-4 fix leaves the other operand sharded on J (call again).
+ * The gather itself is sm_gather_shards with
+ * SM_WHAT_A / SM_WHAT_B into the global layout, whose views serve any
+ * partial gather. Errors: SM_ERR_CASE for case-1/3 plans. */
+int32_t sm_plan_gathered(const sm_plan_t* plan, sm_plan_t* out);
+
 /* Local products C_u = A_u . B_u for units [unit_begin, unit_begin+count):
  * bfloat16 inputs, fp32 accumulation, epilogue, store in plan->out_dtype
  * (learntpu.dev ch05 sandbox "Local matmul"; lingze.zone Case 1 and 3).
@@ -209,6 +220,26 @@ int32_t sm_local_gemm(const sm_plan_t* plan, const sm_buf* A, const sm_buf* B,
 int32_t sm_reduce_partials(const sm_plan_t* plan, const sm_buf* partials,
                            const sm_buf* out, int32_t mode, int32_t group_begin,
                            int32_t group_count, void* stream);
+
+/* Local products and their reduction in one kernel, with no partial buffers
+ * (the one-GPU counterpart of overlapping the reduce with the matmul,
+ * learntpu.dev ch05 "Overlapping communication with compute: collective
+ * matmul"). For each group g in [group_begin, group_begin+count) of a
+ * case-3 plan, the N units' products accumulate into one fp32 accumulator
+ * in rank order y = 0..N-1 -- the N slices of J are contiguous in the
+ * global layout, so this is one product over the whole of J -- and the
+ * finished block S_g is written:
+ *  SM_ALLREDUCE: out global [I,K] at the group's block, or stacked by
+ *    g - group_begin ([m, n] blocks);
+ *  SM_REDUCESCATTER: out global (the same rows, at the plan's c_rs
+ *    coordinates), or stacked by (g - group_begin) * N + y ([m/N, n]).
+ * A and B must use the global layout (block_stride 0). The result equals
+ * sm_local_gemm + sm_reduce_partials up to fp32 summation order (bit for
+ * bit on integer-valued inputs). Local products of at most 16 rows are
+ * refused with SM_ERR_SHAPE (their split-J kernel needs the partials). */
+int32_t sm_local_gemm_reduce(const sm_plan_t* plan, const sm_buf* A, const sm_buf* B,
+                             const sm_buf* out, int32_t mode, int32_t group_begin,
+                             int32_t group_count, void* stream);
 
 /* All-gather on one GPU: copy each distinct finished block once from a
  * stacked layout into the global layout (lingze.zone Case 1, replication

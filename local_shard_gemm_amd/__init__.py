@@ -54,7 +54,7 @@ SM_WHAT_A, SM_WHAT_B, SM_WHAT_C_BLOCKS, SM_WHAT_C_SCATTERED, SM_WHAT_C_PARTIAL =
 EXPORTED = (
     "sm_abi_version", "sm_plan_size", "sm_status_str", "sm_last_error", "sm_mesh_init",
     "sm_parse_spec", "sm_plan", "sm_rank_info", "sm_local_gemm", "sm_reduce_partials",
-    "sm_gather_shards",
+    "sm_gather_shards", "sm_plan_gathered", "sm_local_gemm_reduce",
 )
 
 
@@ -150,6 +150,10 @@ def load(path: str = LIB_PATH):
         lib.sm_reduce_partials.argtypes = [P(sm_plan_t), P(sm_buf), P(sm_buf), i32, i32, i32, vp]
         lib.sm_gather_shards.restype = i32
         lib.sm_gather_shards.argtypes = [P(sm_plan_t), i32, P(sm_buf), P(sm_buf), vp]
+        lib.sm_plan_gathered.restype = i32
+        lib.sm_plan_gathered.argtypes = [P(sm_plan_t), P(sm_plan_t)]
+        lib.sm_local_gemm_reduce.restype = i32
+        lib.sm_local_gemm_reduce.argtypes = [P(sm_plan_t), P(sm_buf), P(sm_buf), P(sm_buf), i32, i32, i32, vp]
         if lib.sm_abi_version() != SM_ABI_VERSION:
             raise ShardmmError(SM_ERR_ARG, "SM_ERR_ARG", "libshardmm ABI version mismatch")
         if lib.sm_plan_size() != ctypes.sizeof(sm_plan_t):
@@ -254,6 +258,21 @@ def sm_reduce_partials(plan: sm_plan_t, partials, out, mode: int = SM_ALLREDUCE,
     p, o = _as_buf(partials), _as_buf(out)
     _check(load().sm_reduce_partials(ctypes.byref(plan), ctypes.byref(p), ctypes.byref(o), mode,
                                      group_begin, group_count, _stream(stream)))
+
+
+def sm_plan_gathered(plan: sm_plan_t) -> sm_plan_t:
+    q = sm_plan_t()
+    _check(load().sm_plan_gathered(ctypes.byref(plan), ctypes.byref(q)))
+    return q
+
+
+def sm_local_gemm_reduce(plan: sm_plan_t, A, B, out, mode: int = SM_ALLREDUCE, group_begin: int = 0,
+                         group_count: Optional[int] = None, stream=None) -> None:
+    if group_count is None:
+        group_count = plan.n_groups - group_begin
+    a, b, o = _as_buf(A), _as_buf(B), _as_buf(out)
+    _check(load().sm_local_gemm_reduce(ctypes.byref(plan), ctypes.byref(a), ctypes.byref(b), ctypes.byref(o),
+                                       mode, group_begin, group_count, _stream(stream)))
 
 
 def sm_gather_shards(plan: sm_plan_t, what: int, shards, out, stream=None) -> None:

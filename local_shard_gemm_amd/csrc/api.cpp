@@ -147,6 +147,8 @@ extern "C" int32_t sm_local_gemm(const sm_plan_t* plan, const sm_buf* A, const s
   L.ldc = C->ld;
   L.epilogue = epilogue == SM_EPI_GELU_TANH ? kEpiGelu : kEpiStore;
   L.out_bf16 = p.out_dtype == SM_BF16 ? 1 : 0;
+  L.split_rows = L.M;  // one plain block per unit
+  L.split_stride = 0;
   L.vec_ok = 1;
   for (const Item& it : items)
     if (reinterpret_cast<uintptr_t>(it.ptrs.a) % 16 || reinterpret_cast<uintptr_t>(it.ptrs.b) % 16) L.vec_ok = 0;
@@ -360,4 +362,104 @@ extern "C" int32_t sm_gather_shards(const sm_plan_t* plan, int32_t what, const s
     jobs.push_back(J);
   }
   return run_jobs(jobs, 1, static_cast<int32_t>(esz), static_cast<hipStream_t>(stream), "sm_gather_shards launch");
+}
+
+extern "C" int32_t sm_local_gemm_reduce(const sm_plan_t* plan, const sm_buf* A, const sm_buf* B, const sm_buf* out,
+                                        int32_t mode, int32_t group_begin, int32_t group_count, void* stream) {
+  clear_error();
+  int32_t st = check_plan(plan);
+  if (st) return st;
+  const sm_plan_t& p = *plan;
+  if (p.kase == SM_CASE2 || p.kase == SM_CASE4)
+    return fail(SM_ERR_NEEDS_GATHER, "all-gather the J-sharded operand first (sm_plan_gathered)");
+  if (p.kase != SM_CASE3) return fail(SM_ERR_CASE, "only case-3 plans have partial sums to reduce");
+  if (mode != SM_ALLREDUCE && mode != SM_REDUCESCATTER) return fail(SM_ERR_ARG, "unknown reduce mode");
+  if (p.in_dtype != SM_BF16 || p.out_dtype != SM_F32) return fail(SM_ERR_DTYPE, "bfloat16 inputs, float32 output");
+  if (group_count < 1 || group_begin < 0 || group_begin > p.n_groups - group_count)
+    return fail(SM_ERR_ARG, "group range outside [0, n_groups)");
+  if ((st = check_buf_basic(A, "A", SM_BF16))) return st;
+  if ((st = check_buf_basic(B, "B", SM_BF16))) return st;
+  if ((st = check_buf_basic(out, "out", SM_F32))) return st;
+  if (A->block_stride != 0 || B->block_stride != 0)
+    return fail(SM_ERR_ARG, "the fused path reads A and B in the global layout (block_stride 0)");
+  if (A->ld < p.J) return fail(SM_ERR_SHAPE, "A: global layout needs ld >= J");
+  if (B->ld < p.K) return fail(SM_ERR_SHAPE, "B: global layout needs ld >= K");
+  const int64_t m = p.c_local[0], n = p.c_local[1], kfull = p.J;
+  const int32_t N = p.n_partials;
+  if (m <= kSkinnyMaxM) return fail(SM_ERR_SHAPE, "skinny products reduce through sm_reduce_partials");
+  if (m > INT32_MAX / 2 || n > INT32_MAX / 2 || kfull > INT32_MAX / 2) return fail(SM_ERR_SHAPE, "shape too large");
+  const bool rs = mode == SM_REDUCESCATTER;
+  if (rs && m % N) return fail(SM_ERR_INDIVISIBLE, "rows of a block do not split N ways");
+  const int64_t orows = rs ? m / N : m;
+  if (out->block_stride == 0) {
+    if (out->ld < p.K) return fail(SM_ERR_SHAPE, "out: global layout needs ld >= K");
+  } else if ((st = check_stacked(out, orows, n, "out"))) {
+    return st;
+  }
+
+  GemmLaunch L;
+  std::memset(&L, 0, sizeof L);
+  L.M = static_cast<int32_t>(m);
+  L.N = static_cast<int32_t>(n);
+  L.K = static_cast<int32_t>(kfull);
+  L.tiles_m = static_cast<int32_t>((m + kTileM - 1) / kTileM);
+  L.tiles_n = static_cast<int32_t>((n + kTileN - 1) / kTileN);
+  L.lda = A->ld;
+  L.ldb = B->ld;
+  L.ldc = out->ld;
+  L.epilogue = kEpiStore;
+  L.out_bf16 = 0;
+  const bool split = rs && out->block_stride != 0;
+  L.split_rows = split ? static_cast<int32_t>(orows) : L.M;
+  L.split_stride = split ? out->block_stride : 0;
+  L.vec_ok = 1;
+
+  struct Item {
+    int32_t b_id, a_row;
+    GemmUnitPtrs ptrs;
+  };
+  std::vector<Item> items;
+  for (int32_t g = group_begin; g < group_begin + group_count; ++g) {
+    // Rank order y = 0..N-1 covers J contiguously in both operands.
+    UnitView v;
+    if ((st = unit_view(p, g * N, &v))) return st;
+    if (v.a_col0 != 0 || v.b_row0 != 0) return fail(SM_ERR_ARG, "J slices are not contiguous from 0");
+    BlockRef ra{v.a_row0 * A->ld, m, kfull};
+    BlockRef rb{v.b_col0, kfull, n};
+    if ((st = check_extent(A, ra, "A"))) return st;
+    if ((st = check_extent(B, rb, "B"))) return st;
+    int64_t coff;
+    if (out->block_stride == 0) {
+      coff = v.c_row0 * out->ld + v.c_col0;
+      BlockRef rc{coff, m, n};
+      if ((st = check_extent(out, rc, "out"))) return st;
+    } else {
+      const int32_t nblk = rs ? N : 1;
+      coff = static_cast<int64_t>(g - group_begin) * nblk * out->block_stride;
+      for (int32_t y = 0; y < nblk; ++y) {
+        BlockRef rc{coff + y * out->block_stride, orows, n};
+        if ((st = check_extent(out, rc, "out"))) return st;
+      }
+    }
+    Item it;
+    it.b_id = v.b_block[1];
+    it.a_row = v.a_block[0];
+    it.ptrs.a = static_cast<const uint16_t*>(A->ptr) + ra.offset;
+    it.ptrs.b = static_cast<const uint16_t*>(B->ptr) + rb.offset;
+    it.ptrs.c = static_cast<float*>(out->ptr) + coff;
+    if (reinterpret_cast<uintptr_t>(it.ptrs.a) % 16 || reinterpret_cast<uintptr_t>(it.ptrs.b) % 16) L.vec_ok = 0;
+    items.push_back(it);
+  }
+  std::stable_sort(items.begin(), items.end(), [](const Item& x, const Item& y) {
+    return x.b_id != y.b_id ? x.b_id < y.b_id : x.a_row < y.a_row;
+  });
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  for (size_t first = 0; first < items.size(); first += kMaxUnitsPerLaunch) {
+    const size_t cnt = std::min(items.size() - first, static_cast<size_t>(kMaxUnitsPerLaunch));
+    L.n_units = static_cast<int32_t>(cnt);
+    for (size_t i = 0; i < cnt; ++i) L.u[i] = items[first + i].ptrs;
+    hipError_t e = launch_gemm_mfma(L, s);
+    if (e != hipSuccess) return hip_fail(e, "sm_local_gemm_reduce launch");
+  }
+  return SM_OK;
 }

@@ -122,11 +122,14 @@ __device__ __forceinline__ void tile_of(int w, int T, int VR, int VC, int* vr, i
 }
 
 template <bool OUT_BF16, bool GELU, bool EDGE>
-__device__ __forceinline__ void store_tile(const f32x16 (&acc)[4][4], void* C, int64_t ldc, int row0,
-                                           int col0, int M, int N) {
+__device__ __forceinline__ void store_tile(const f32x16 (&acc)[4][4], void* C, const GemmLaunch& L, int row0,
+                                           int col0) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const int rsub = 4 * (lane >> 5), csub = lane & 31;
+  const int M = L.M, N = L.N;
+  const int64_t ldc = L.ldc;
+  const bool split = L.split_rows < M;
 #pragma unroll
   for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
@@ -138,7 +141,8 @@ __device__ __forceinline__ void store_tile(const f32x16 (&acc)[4][4], void* C, i
         if (EDGE && (r >= M || c >= N)) continue;
         float x = acc[mi][ni][v];
         if (GELU) x = gelu_tanh_f32(x);
-        const int64_t off = static_cast<int64_t>(r) * ldc + c;
+        const int64_t off = split ? (r / L.split_rows) * L.split_stride + static_cast<int64_t>(r % L.split_rows) * ldc + c
+                                  : static_cast<int64_t>(r) * ldc + c;
         if (OUT_BF16)
           static_cast<uint16_t*>(C)[off] = bf16_rne(x);
         else
@@ -239,7 +243,7 @@ __device__ __forceinline__ void run_tile(const GemmLaunch& L, const uint16_t* __
     __syncthreads();
   }
 
-  store_tile<OUT_BF16, GELU, EDGE>(acc, C, L.ldc, row0, col0, M, N);
+  store_tile<OUT_BF16, GELU, EDGE>(acc, C, L, row0, col0);
 }
 
 // ---------------------------------------------------------------------------
@@ -483,7 +487,7 @@ __device__ __forceinline__ void run_tile_lds(const GemmLaunch& L, const uint16_t
   }
   mma(F1);
 
-  store_tile<OUT_BF16, GELU, false>(acc, C, L.ldc, row0, col0, L.M, L.N);
+  store_tile<OUT_BF16, GELU, false>(acc, C, L, row0, col0);
 }
 
 // Interior tiles: every tile of the launch is a full BM x BN tile, K is a

@@ -28,6 +28,10 @@ struct GemmLaunch {
   int32_t epilogue;          // kEpiStore / kEpiGelu
   int32_t out_bf16;          // 1: store bfloat16 (RNE), 0: float32
   int32_t vec_ok;            // 1: every A/B view starts 16-byte aligned
+  // Output rows in blocks: row r goes to c + (r / split_rows) * split_stride
+  // + (r % split_rows) * ldc (split_rows >= M: one plain [M, N] block).
+  int32_t split_rows;
+  int64_t split_stride;
   GemmUnitPtrs u[kMaxUnitsPerLaunch];  // in scheduling order
 };
 

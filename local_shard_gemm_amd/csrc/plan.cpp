@@ -422,6 +422,30 @@ int32_t sm_plan(const sm_mesh* mesh, const sm_spec* a, const sm_spec* b, int64_t
   return SM_OK;
 }
 
+int32_t sm_plan_gathered(const sm_plan_t* plan, sm_plan_t* out) {
+  clear_error();
+  int32_t st = check_plan(plan);
+  if (st) return st;
+  if (!out) return fail(SM_ERR_ARG, "NULL output");
+  if (plan->kase != SM_CASE2 && plan->kase != SM_CASE4)
+    return fail(SM_ERR_CASE, "only case-2 and case-4 plans need an operand gathered");
+  // The gathered operand loses the gather axes from both of its dims.
+  sm_spec a = plan->a, b = plan->b;
+  sm_spec& g = plan->gather_operand == 0 ? a : b;
+  for (int32_t d = 0; d < 2; ++d) {
+    int32_t kept = 0;
+    for (int32_t k = 0; k < g.n[d]; ++k)
+      if (!(plan->gather_axes & (1u << g.axes[d][k]))) g.axes[d][kept++] = g.axes[d][k];
+    for (int32_t k = kept; k < SM_MAX_AXES; ++k) g.axes[d][k] = 0;
+    g.n[d] = kept;
+  }
+  sm_plan_t q;
+  if ((st = sm_plan(&plan->mesh, &a, &b, plan->I, plan->J, plan->K, plan->in_dtype, plan->out_dtype, &q)))
+    return st;
+  *out = q;  // case 1 or 3; case 2 again when the other operand is J-sharded
+  return SM_OK;
+}
+
 int32_t sm_rank_info(const sm_plan_t* plan, int32_t rank, sm_rank_info_t* out) {
   clear_error();
   int32_t st = check_plan(plan);

@@ -337,6 +337,23 @@ def plan(mesh, a, b, I: int, J: int, K: int, in_dtype: str = "bf16", out_dtype: 
     )
 
 
+def gathered(p: Plan) -> Plan:
+    """The plan after the case-2 / case-4 fix: all-gather ``p.gather_operand``
+    over ``p.gather_axes`` (lingze.zone "Case 2" and "Case 4"; learntpu.dev
+    ch05, the four cases), i.e. drop those axes from that operand's spec and
+    plan again."""
+    if p.case not in (2, 4):
+        raise PlanError("CASE", "nothing to gather")
+    drop = set(p.gather_axes)
+
+    def strip(spec: Spec) -> Spec:
+        return (tuple(a for a in spec[0] if a not in drop), tuple(a for a in spec[1] if a not in drop))
+
+    a = strip(p.a) if p.gather_operand == "A" else p.a
+    b = strip(p.b) if p.gather_operand == "B" else p.b
+    return plan(p.mesh, a, b, p.I, p.J, p.K, p.in_dtype, p.out_dtype)
+
+
 def notation(name: str, spec: Spec, dims=("I", "J"), unreduced: Tuple[str, ...] = ()) -> str:
     """Subscript notation of the pages, e.g. A[I_X, J_Y]{U_Y}."""
     parts = []

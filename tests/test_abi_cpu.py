@@ -125,6 +125,29 @@ def _compare(mesh_axes, a, b, I, J, K):
         assert got_err == _CODE[want_err], (mesh_axes, a, b)
         return
     assert got_err is None, (mesh_axes, a, b, got_err)
+    _compare_plans(got, want, names)
+    if want.case in (2, 4):
+        # the case-2/4 fix by composition: plan after gathering the operand
+        try:
+            want_g, want_g_err = ref_planner.gathered(want), None
+        except ref_planner.PlanError as e:
+            want_g, want_g_err = None, e.code
+        try:
+            got_g, got_g_err = sm.sm_plan_gathered(got), None
+        except sm.ShardmmError as e:
+            got_g, got_g_err = None, e.status
+        if want_g_err is not None:
+            assert got_g_err == _CODE[want_g_err], (mesh_axes, a, b)
+        else:
+            assert got_g_err is None, (mesh_axes, a, b, got_g_err)
+            _compare_plans(got_g, want_g, names)
+    else:
+        with pytest.raises(sm.ShardmmError) as ei:
+            sm.sm_plan_gathered(got)
+        assert ei.value.status == sm.SM_ERR_CASE
+
+
+def _compare_plans(got, want, names):
     assert got.kase == want.case
     assert got.n_ranks == want.n_ranks
     assert tuple(got.a_local) == want.a_local and tuple(got.b_local) == want.b_local
@@ -232,6 +255,40 @@ def test_local_gemm_validation():
     assert _err(sm.sm_local_gemm, p1, A, B, _fb(60)) == sm.SM_ERR_SHAPE
     bad = sm.sm_plan_t()
     assert _err(sm.sm_local_gemm, bad, A, B, Cs) == sm.SM_ERR_ARG
+
+
+def test_gathered_plan_examples():
+    """lingze.zone 'Case 2': A[I,J_X].B[J,K] -> gather A -> case 1;
+    'Case 4': A[I_X,J].B[J,K_X] -> gather the smaller operand -> case 1."""
+    p2 = sm.sm_plan({"X": 4}, "A[I, J_X]", "B[J, K]", 64, 64, 64)
+    q2 = sm.sm_plan_gathered(p2)
+    assert p2.kase == sm.SM_CASE2 and q2.kase == sm.SM_CASE1 and q2.a.dims() == ((), ())
+    p4 = sm.sm_plan({"X": 4}, "A[I_X, J]", "B[J, K_X]", 64, 32, 128)
+    assert p4.kase == sm.SM_CASE4 and p4.gather_operand == 0  # A (64x32) smaller than B (32x128)
+    q4 = sm.sm_plan_gathered(p4)
+    assert q4.kase == sm.SM_CASE1 and q4.n_groups == 4
+    # case 4 whose fix leaves A J-sharded: case 2 next, then case 1
+    p = sm.sm_plan({"X": 2, "Y": 2}, "A[I_X, J_Y]", "B[J, K_X]", 16, 16, 32)
+    q = sm.sm_plan_gathered(p)
+    assert p.kase == sm.SM_CASE4 and q.kase == sm.SM_CASE2
+    assert sm.sm_plan_gathered(q).kase == sm.SM_CASE1
+
+
+def test_fused_reduce_validation():
+    p3 = sm.sm_plan({"X": 2}, "P(None, 'X')", "P('X', None)", 64, 128, 64)
+    p1 = sm.sm_plan({"X": 2}, "P('X', None)", "P()", 64, 128, 64)
+    p2 = sm.sm_plan({"X": 2}, "P(None, 'X')", "P()", 64, 128, 64)
+    sk = sm.sm_plan({"X": 2}, "P(None, 'X')", "P('X', None)", 16, 128, 64)
+    A, B, out = _fb(128), _fb(64), _fb(64)
+    assert _err(sm.sm_local_gemm_reduce, p1, A, B, out) == sm.SM_ERR_CASE
+    assert _err(sm.sm_local_gemm_reduce, p2, A, B, out) == sm.SM_ERR_NEEDS_GATHER
+    assert _err(sm.sm_local_gemm_reduce, p3, _fb(128, 64 * 128), B, out) == sm.SM_ERR_ARG
+    assert _err(sm.sm_local_gemm_reduce, sk, A, B, out) == sm.SM_ERR_SHAPE
+    assert _err(sm.sm_local_gemm_reduce, p3, A, B, out, 9) == sm.SM_ERR_ARG
+    assert _err(sm.sm_local_gemm_reduce, p3, A, B, _fb(64, 16 * 64, elems=2 * 16 * 64), sm.SM_REDUCESCATTER) \
+        == sm.SM_ERR_SHAPE
+    q = sm.sm_plan({"X": 3}, "P(None, 'X')", "P('X', None)", 64, 96, 64)
+    assert _err(sm.sm_local_gemm_reduce, q, _fb(96), B, out, sm.SM_REDUCESCATTER) == sm.SM_ERR_INDIVISIBLE
 
 
 def test_reduce_and_gather_validation():
