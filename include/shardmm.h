@@ -241,6 +241,37 @@ int32_t sm_local_gemm_reduce(const sm_plan_t* plan, const sm_buf* A, const sm_bu
                              const sm_buf* out, int32_t mode, int32_t group_begin,
                              int32_t group_count, void* stream);
 
+/* Sequence-parallel tail (ana-alekseeva.com "Sequence parallelism": the
+ * all-reduce of a tensor-parallel block becomes a reduce-scatter, layer norm
+ * runs on each device's own token rows, and the rows are all-gathered before
+ * the next block). For each group g, reduce the N partials in rank order
+ * exactly as sm_reduce_partials(SM_REDUCESCATTER) and apply, to every owned
+ * row x of length n:
+ *   y = (x - mean(x)) / sqrt(var(x) + eps) * gamma + beta,
+ * var the biased (1/n) variance, gamma/beta device float arrays of n
+ * elements (NULL = 1 / 0). The plan's output must have whole rows
+ * (c_grid[1] == 1, else SM_ERR_CASE); rows of at most 32768 elements, n a
+ * multiple of 4 and 16-byte aligned rows (SM_ERR_SHAPE / SM_ERR_ALIGN).
+ * out: global layout (then the all-gathered tensor is already in place) or
+ * stacked by (g - group_begin) * N + y. */
+int32_t sm_reduce_scatter_layernorm(const sm_plan_t* plan, const sm_buf* partials,
+                                    const sm_buf* out, const float* gamma, const float* beta,
+                                    float eps, int32_t group_begin, int32_t group_count,
+                                    void* stream);
+
+/* Reshard a 2-D array between two partition specs on one mesh: AllToAll
+ * A[I, J_X] -> A[I_X, J] moves which dimension is sharded (learntpu.dev
+ * ch05, table of the four collectives; lingze.zone "Communication
+ * primitives"); a replicated target ("P()") is an all-gather. Every block
+ * of `to` is assembled from the overlapping parts of the blocks of `from`.
+ * src / dst: global layout (block_stride 0) or stacked by block id
+ * (row_block * grid[1] + col_block), one copy per distinct block.
+ * dtype: SM_BF16 or SM_F32. Errors: SM_ERR_SPEC, SM_ERR_AXIS_REUSED,
+ * SM_ERR_INDIVISIBLE as for sm_plan; SM_ERR_ARG if both are global. */
+int32_t sm_reshard(const sm_mesh* mesh, const sm_spec* from, const sm_spec* to,
+                   int64_t rows, int64_t cols, int32_t dtype, const sm_buf* src,
+                   const sm_buf* dst, void* stream);
+
 /* All-gather on one GPU: copy each distinct finished block once from a
  * stacked layout into the global layout (lingze.zone Case 1, replication
  * as a separate AllGather; semiaifoundry.com step 5). what = SM_WHAT_A /

@@ -54,7 +54,8 @@ SM_WHAT_A, SM_WHAT_B, SM_WHAT_C_BLOCKS, SM_WHAT_C_SCATTERED, SM_WHAT_C_PARTIAL =
 EXPORTED = (
     "sm_abi_version", "sm_plan_size", "sm_status_str", "sm_last_error", "sm_mesh_init",
     "sm_parse_spec", "sm_plan", "sm_rank_info", "sm_local_gemm", "sm_reduce_partials",
-    "sm_gather_shards", "sm_plan_gathered", "sm_local_gemm_reduce",
+    "sm_gather_shards", "sm_plan_gathered", "sm_local_gemm_reduce", "sm_reduce_scatter_layernorm",
+    "sm_reshard",
 )
 
 
@@ -154,6 +155,11 @@ def load(path: str = LIB_PATH):
         lib.sm_plan_gathered.argtypes = [P(sm_plan_t), P(sm_plan_t)]
         lib.sm_local_gemm_reduce.restype = i32
         lib.sm_local_gemm_reduce.argtypes = [P(sm_plan_t), P(sm_buf), P(sm_buf), P(sm_buf), i32, i32, i32, vp]
+        lib.sm_reduce_scatter_layernorm.restype = i32
+        lib.sm_reduce_scatter_layernorm.argtypes = [P(sm_plan_t), P(sm_buf), P(sm_buf), vp, vp, ctypes.c_float,
+                                                    i32, i32, vp]
+        lib.sm_reshard.restype = i32
+        lib.sm_reshard.argtypes = [P(sm_mesh), P(sm_spec), P(sm_spec), i64, i64, i32, P(sm_buf), P(sm_buf), vp]
         if lib.sm_abi_version() != SM_ABI_VERSION:
             raise ShardmmError(SM_ERR_ARG, "SM_ERR_ARG", "libshardmm ABI version mismatch")
         if lib.sm_plan_size() != ctypes.sizeof(sm_plan_t):
@@ -273,6 +279,31 @@ def sm_local_gemm_reduce(plan: sm_plan_t, A, B, out, mode: int = SM_ALLREDUCE, g
     a, b, o = _as_buf(A), _as_buf(B), _as_buf(out)
     _check(load().sm_local_gemm_reduce(ctypes.byref(plan), ctypes.byref(a), ctypes.byref(b), ctypes.byref(o),
                                        mode, group_begin, group_count, _stream(stream)))
+
+
+def sm_reduce_scatter_layernorm(plan: sm_plan_t, partials, out, gamma=None, beta=None, eps: float = 1e-5,
+                                group_begin: int = 0, group_count: Optional[int] = None, stream=None) -> None:
+    """gamma / beta: float32 device tensors of the row length, or None."""
+    if group_count is None:
+        group_count = plan.n_groups - group_begin
+    p, o = _as_buf(partials), _as_buf(out)
+    g = ctypes.c_void_p(gamma.data_ptr() if gamma is not None else 0)
+    b = ctypes.c_void_p(beta.data_ptr() if beta is not None else 0)
+    _check(load().sm_reduce_scatter_layernorm(ctypes.byref(plan), ctypes.byref(p), ctypes.byref(o), g, b,
+                                              float(eps), group_begin, group_count, _stream(stream)))
+
+
+def sm_reshard(mesh, frm, to, rows: int, cols: int, dtype: int, src, dst, stream=None) -> None:
+    """``mesh``: sm_mesh or {name: size}; ``frm`` / ``to``: sm_spec or spec text."""
+    if not isinstance(mesh, sm_mesh):
+        mesh = sm_mesh_init(mesh)
+    if isinstance(frm, str):
+        frm = sm_parse_spec(mesh, frm)
+    if isinstance(to, str):
+        to = sm_parse_spec(mesh, to)
+    s, d = _as_buf(src), _as_buf(dst)
+    _check(load().sm_reshard(ctypes.byref(mesh), ctypes.byref(frm), ctypes.byref(to), rows, cols, dtype,
+                             ctypes.byref(s), ctypes.byref(d), _stream(stream)))
 
 
 def sm_gather_shards(plan: sm_plan_t, what: int, shards, out, stream=None) -> None:

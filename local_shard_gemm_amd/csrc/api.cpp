@@ -13,13 +13,6 @@
 #include "kernels.h"
 
 namespace shardmm {
-namespace {
-
-// Describes how one logical block of a buffer is addressed.
-struct BlockRef {
-  int64_t offset;  // element offset of the block's (0,0)
-  int64_t rows, cols;
-};
 
 int32_t check_buf_basic(const sm_buf* b, const char* what, int32_t dtype) {
   if (!b) return fail(SM_ERR_ARG, std::string(what) + ": NULL sm_buf");
@@ -59,7 +52,6 @@ int32_t hip_fail(hipError_t e, const char* where) {
   return fail(SM_ERR_HIP, std::string(where) + ": " + hipGetErrorString(e));
 }
 
-}  // namespace
 }  // namespace shardmm
 
 using namespace shardmm;
@@ -164,7 +156,7 @@ extern "C" int32_t sm_local_gemm(const sm_plan_t* plan, const sm_buf* A, const s
   return SM_OK;
 }
 
-namespace {
+namespace shardmm {
 
 // 16-byte vectors need aligned row starts in every source and the target.
 void set_vec_flags(std::vector<RowJob>& jobs, int32_t elem_bytes) {
@@ -209,7 +201,7 @@ int32_t run_jobs(std::vector<RowJob>& jobs, int32_t n_sum, int32_t elem_bytes, h
   return SM_OK;
 }
 
-}  // namespace
+}  // namespace shardmm
 
 extern "C" int32_t sm_reduce_partials(const sm_plan_t* plan, const sm_buf* partials, const sm_buf* out,
                                       int32_t mode, int32_t group_begin, int32_t group_count, void* stream) {

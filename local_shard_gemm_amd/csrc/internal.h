@@ -29,6 +29,23 @@ int32_t unit_view(const sm_plan_t& p, int32_t unit, UnitView* out);
 
 int32_t check_plan(const sm_plan_t* p);
 
+// Axis indices in range and no axis on two dims (SM_ERR_SPEC / SM_ERR_AXIS_REUSED).
+int32_t validate_spec(const sm_mesh& mesh, const sm_spec& s, const char* what);
+
 size_t dtype_size(int32_t dt);
+
+// ---- buffer checks and row-job launches shared by the device entry points
+
+// One logical block of a buffer: element offset of its (0,0) and its extent.
+struct BlockRef {
+  int64_t offset;
+  int64_t rows, cols;
+};
+// Pointer, alignment, ld, block_stride and elems of one sm_buf.
+int32_t check_buf_basic(const sm_buf* b, const char* what, int32_t dtype);
+// The block lies inside the buffer.
+int32_t check_extent(const sm_buf* b, const BlockRef& r, const char* what);
+// Stacked blocks of rows x cols do not overlap.
+int32_t check_stacked(const sm_buf* b, int64_t rows, int64_t cols, const char* what);
 
 }  // namespace shardmm

@@ -5,6 +5,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <vector>
 
 namespace shardmm {
 
@@ -59,6 +60,16 @@ struct RowLaunch {
 hipError_t launch_gemm_mfma(const GemmLaunch& L, hipStream_t s);
 hipError_t launch_gemm_skinny(const GemmLaunch& L, hipStream_t s);
 hipError_t launch_rows(const RowLaunch& L, hipStream_t s);
+// Host side: launch row jobs (rank-ordered sums when n_sum > 1, copies when
+// n_sum == 1) in batches of kMaxJobsPerLaunch; returns an sm_status.
+int32_t run_jobs(std::vector<RowJob>& jobs, int32_t n_sum, int32_t elem_bytes, hipStream_t s, const char* where);
+// SM_ERR_HIP with the runtime's text.
+int32_t hip_fail(hipError_t e, const char* where);
+// Rank-ordered reduce of whole rows followed by a layer norm of each row
+// (float32 only, 16-byte vectors, rows of at most 32768 elements).
+hipError_t launch_rows_layernorm(const RowLaunch& L, const float* gamma, const float* beta, float eps,
+                                 hipStream_t s);
+constexpr int kLayerNormMaxCols = 32768;
 
 // Tile sizes of the MFMA kernel (host side uses them for the grid).
 constexpr int kTileM = 256, kTileN = 256, kTileK = 64;

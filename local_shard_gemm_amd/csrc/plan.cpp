@@ -292,7 +292,7 @@ int32_t sm_parse_spec(const sm_mesh* mesh, const char* text, sm_spec* out) {
   return SM_OK;
 }
 
-static int32_t validate_spec(const sm_mesh& mesh, const sm_spec& s, const char* what) {
+static int32_t validate_spec_impl(const sm_mesh& mesh, const sm_spec& s, const char* what) {
   uint32_t used = 0;
   for (int32_t d = 0; d < 2; ++d) {
     if (s.n[d] < 0 || s.n[d] > SM_MAX_AXES) return fail(SM_ERR_SPEC, std::string(what) + ": bad axis count");
@@ -344,8 +344,8 @@ int32_t sm_plan(const sm_mesh* mesh, const sm_spec* a, const sm_spec* b, int64_t
   for (int32_t x = 0; x < mesh->n_axes; ++x)
     if (mesh->sizes[x] < 1) return fail(SM_ERR_MESH, "axis sizes must be >= 1");
   int32_t st;
-  if ((st = validate_spec(*mesh, *a, "A"))) return st;
-  if ((st = validate_spec(*mesh, *b, "B"))) return st;
+  if ((st = validate_spec_impl(*mesh, *a, "A"))) return st;
+  if ((st = validate_spec_impl(*mesh, *b, "B"))) return st;
   if (I < 1 || J < 1 || K < 1) return fail(SM_ERR_SHAPE, "I, J and K must be >= 1");
   if (I > (int64_t(1) << 40) || J > (int64_t(1) << 40) || K > (int64_t(1) << 40))
     return fail(SM_ERR_SHAPE, "dimension too large");
@@ -486,3 +486,7 @@ int32_t sm_rank_info(const sm_plan_t* plan, int32_t rank, sm_rank_info_t* out) {
 }
 
 }  // extern "C"
+
+int32_t shardmm::validate_spec(const sm_mesh& mesh, const sm_spec& s, const char* what) {
+  return validate_spec_impl(mesh, s, what);
+}

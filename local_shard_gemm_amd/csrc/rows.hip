@@ -153,7 +153,105 @@ __global__ __launch_bounds__(NT) void rows_b16_copy_kernel(const RowLaunch L) {
     copy_row_16_scalar(J, row);
 }
 
+// Sum of one float per thread over the workgroup, in a fixed order (wave
+// butterflies, then the 4 wave totals in wave order): deterministic.
+__device__ __forceinline__ float block_sum(float x, float* red) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o, 64);
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = x;
+  __syncthreads();
+  float t = red[0];
+#pragma unroll
+  for (int w = 1; w < NT / 64; ++w) t += red[w];
+  return t;
+}
+
+// Rank-ordered sum of the partials of one row, then layer norm of the row:
+// y = (x - mean) / sqrt(var + eps) * gamma + beta (biased variance). The
+// whole row stays in registers: V float4 per thread (n <= 1024 V).
+template <int NS, int V>
+__global__ __launch_bounds__(NT) void rows_layernorm_kernel(const RowLaunch L, const float* __restrict__ gamma,
+                                                            const float* __restrict__ beta, float eps) {
+  __shared__ float red[NT / 64];
+  const RowJob& J = L.jobs[blockIdx.y];
+  const int row = blockIdx.x;
+  if (row >= J.rows) return;
+  const int nsum = NS > 0 ? NS : L.n_sum;
+  const float* src = static_cast<const float*>(J.src) + static_cast<int64_t>(row) * J.lds;
+  float* dst = static_cast<float*>(J.dst) + static_cast<int64_t>(row) * J.ldd;
+  const int n4 = J.cols >> 2;
+  float4 v[V];
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < V; ++i) {
+    const int c4 = threadIdx.x + i * NT;
+    v[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (c4 < n4) {
+      v[i] = ldnt(reinterpret_cast<const float4*>(src) + c4);
+      for (int y = 1; y < nsum; ++y) add4(v[i], ldnt(reinterpret_cast<const float4*>(src + y * J.src_stride) + c4));
+      s += (v[i].x + v[i].y) + (v[i].z + v[i].w);
+    }
+  }
+  const float inv_n = 1.0f / static_cast<float>(J.cols);
+  const float mean = block_sum(s, red) * inv_n;
+  float q = 0.f;
+#pragma unroll
+  for (int i = 0; i < V; ++i) {
+    const int c4 = threadIdx.x + i * NT;
+    if (c4 < n4) {
+      const float a = v[i].x - mean, b = v[i].y - mean, c = v[i].z - mean, d = v[i].w - mean;
+      q += (a * a + b * b) + (c * c + d * d);
+    }
+  }
+  const float var = block_sum(q, red) * inv_n;
+  const float rstd = 1.0f / sqrtf(var + eps);
+#pragma unroll
+  for (int i = 0; i < V; ++i) {
+    const int c4 = threadIdx.x + i * NT;
+    if (c4 < n4) {
+      float4 g = make_float4(1.f, 1.f, 1.f, 1.f), b = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (gamma) g = reinterpret_cast<const float4*>(gamma)[c4];
+      if (beta) b = reinterpret_cast<const float4*>(beta)[c4];
+      float4 o;
+      o.x = (v[i].x - mean) * rstd * g.x + b.x;
+      o.y = (v[i].y - mean) * rstd * g.y + b.y;
+      o.z = (v[i].z - mean) * rstd * g.z + b.z;
+      o.w = (v[i].w - mean) * rstd * g.w + b.w;
+      stnt(reinterpret_cast<float4*>(dst) + c4, o);
+    }
+  }
+}
+
+template <int V>
+void launch_ln_v(const RowLaunch& L, const float* gamma, const float* beta, float eps, hipStream_t s) {
+  dim3 grid(L.max_rows, L.n_jobs);
+  switch (L.n_sum) {
+    case 1: hipLaunchKernelGGL((rows_layernorm_kernel<1, V>), grid, dim3(NT), 0, s, L, gamma, beta, eps); break;
+    case 2: hipLaunchKernelGGL((rows_layernorm_kernel<2, V>), grid, dim3(NT), 0, s, L, gamma, beta, eps); break;
+    case 4: hipLaunchKernelGGL((rows_layernorm_kernel<4, V>), grid, dim3(NT), 0, s, L, gamma, beta, eps); break;
+    case 8: hipLaunchKernelGGL((rows_layernorm_kernel<8, V>), grid, dim3(NT), 0, s, L, gamma, beta, eps); break;
+    default: hipLaunchKernelGGL((rows_layernorm_kernel<0, V>), grid, dim3(NT), 0, s, L, gamma, beta, eps); break;
+  }
+}
+
 }  // namespace
+
+hipError_t launch_rows_layernorm(const RowLaunch& L, const float* gamma, const float* beta, float eps,
+                                 hipStream_t s) {
+  if (L.n_jobs <= 0 || L.max_rows <= 0) return hipSuccess;
+  int max_cols = 0;
+  for (int i = 0; i < L.n_jobs; ++i) max_cols = max(max_cols, L.jobs[i].cols);
+  const int per = (max_cols / 4 + NT - 1) / NT;  // float4 per thread
+  if (per <= 1) launch_ln_v<1>(L, gamma, beta, eps, s);
+  else if (per <= 2) launch_ln_v<2>(L, gamma, beta, eps, s);
+  else if (per <= 4) launch_ln_v<4>(L, gamma, beta, eps, s);
+  else if (per <= 8) launch_ln_v<8>(L, gamma, beta, eps, s);
+  else if (per <= 16) launch_ln_v<16>(L, gamma, beta, eps, s);
+  else if (per <= 32) launch_ln_v<32>(L, gamma, beta, eps, s);
+  else return hipErrorInvalidValue;
+  return hipGetLastError();
+}
 
 hipError_t launch_rows(const RowLaunch& L, hipStream_t s) {
   if (L.n_jobs <= 0 || L.max_rows <= 0 || L.n_chunks <= 0) return hipSuccess;

@@ -337,6 +337,21 @@ def plan(mesh, a, b, I: int, J: int, K: int, in_dtype: str = "bf16", out_dtype: 
     )
 
 
+def array_blocks(mesh, spec, rows: int, cols: int):
+    """Distinct blocks of one 2-D array under a spec: {block_id: (r0, c0,
+    rows, cols)}, block_id = row_block * grid[1] + col_block (learntpu.dev
+    ch05 sandbox: "A: 4 x 2 blocks of [2048, 14336]")."""
+    mesh = _validate_mesh(mesh)
+    sizes = dict(mesh)
+    if isinstance(spec, str):
+        spec = parse_spec(spec)
+    spec = (tuple(spec[0]), tuple(spec[1]))
+    _validate_spec(spec, sizes, "array")
+    br, gr = _split(rows, spec[0], sizes, "rows")
+    bc, gc = _split(cols, spec[1], sizes, "cols")
+    return {i * gc + j: (i * br, j * bc, br, bc) for i in range(gr) for j in range(gc)}
+
+
 def gathered(p: Plan) -> Plan:
     """The plan after the case-2 / case-4 fix: all-gather ``p.gather_operand``
     over ``p.gather_axes`` (lingze.zone "Case 2" and "Case 4"; learntpu.dev

@@ -303,6 +303,59 @@ def mlp_chain(plan1: Plan, plan2: Plan, X, W1, W2, rows=None):
     return H, sum_ranked(zs)
 
 
+# ------------------------------------------------- sequence-parallel tail
+
+def layer_norm(x: np.ndarray, gamma=None, beta=None, eps: float = 1e-5) -> np.ndarray:
+    """Row-wise layer norm in fp64: (x - mean) / sqrt(var + eps) * gamma +
+    beta, with the biased (1/n) variance (Ba, Kiros & Hinton 2016; the pages
+    apply layer norm per token between the reduce-scatter and the
+    all-gather -- ana-alekseeva.com, "Sequence parallelism")."""
+    x = np.asarray(x, dtype=np.float64)
+    n = x.shape[-1]
+    mean = x.sum(axis=-1, keepdims=True) / n
+    d = x - mean
+    var = (d * d).sum(axis=-1, keepdims=True) / n
+    y = d / np.sqrt(var + eps)
+    if gamma is not None:
+        y = y * np.asarray(gamma, dtype=np.float64)
+    if beta is not None:
+        y = y + np.asarray(beta, dtype=np.float64)
+    return y
+
+
+def sp_tail(plan: Plan, parts, gamma=None, beta=None, eps: float = 1e-5) -> np.ndarray:
+    """Reduce-scatter, layer norm of each owned row, all-gather: the global
+    [I, K] result every rank holds afterwards."""
+    rs = reduce_scatter(plan, parts)
+    normed = {key: layer_norm(blk, gamma, beta, eps) for key, blk in rs.items()}
+    return gather_scattered(plan, normed)
+
+
+# ------------------------------------------------------------- resharding
+
+def shard(X: np.ndarray, mesh, spec) -> Dict[int, np.ndarray]:
+    """The distinct blocks of X under a spec, by block id."""
+    from .planner import array_blocks
+
+    return {b: X[r0:r0 + nr, c0:c0 + nc].copy() for b, (r0, c0, nr, nc) in
+            array_blocks(mesh, spec, X.shape[0], X.shape[1]).items()}
+
+
+def unshard(blocks: Dict[int, np.ndarray], mesh, spec, rows: int, cols: int) -> np.ndarray:
+    from .planner import array_blocks
+
+    out = np.zeros((rows, cols), dtype=next(iter(blocks.values())).dtype)
+    for b, (r0, c0, nr, nc) in array_blocks(mesh, spec, rows, cols).items():
+        out[r0:r0 + nr, c0:c0 + nc] = blocks[b]
+    return out
+
+
+def reshard(blocks: Dict[int, np.ndarray], mesh, frm, to, rows: int, cols: int) -> Dict[int, np.ndarray]:
+    """Blocks under `to` from blocks under `frm` (AllToAll when the sharded
+    dimension moves; AllGather when `to` is replicated)."""
+    return shard(unshard(blocks, mesh, frm, rows, cols), mesh, to)
+
+
 # ------------------------------------------------------------------- checks
 
 def freivalds(A, a_view, B, b_view, C: np.ndarray, trials: int = 2, seed: int = 0,

@@ -308,3 +308,22 @@ def test_reduce_and_gather_validation():
     assert _err(sm.sm_gather_shards, p1, sm.SM_WHAT_C_BLOCKS, _fb(8), out) == sm.SM_ERR_ARG
     assert _err(sm.sm_gather_shards, p1, sm.SM_WHAT_C_BLOCKS, _fb(8, 32), _fb(8, 64)) == sm.SM_ERR_ARG
     assert _err(sm.sm_gather_shards, p1, sm.SM_WHAT_C_BLOCKS, _fb(8, 32), _fb(4)) == sm.SM_ERR_SHAPE
+
+
+def test_sp_tail_and_reshard_validation():
+    p3 = sm.sm_plan({"X": 2, "Y": 2}, "P('X', 'Y')", "P('Y', None)", 16, 16, 8)
+    p1 = sm.sm_plan({"X": 2}, "P('X', None)", "P()", 8, 8, 8)
+    pk = sm.sm_plan({"X": 2, "Y": 2}, "P(None, 'Y')", "P('Y', 'X')", 16, 16, 8)
+    parts, out = _fb(8, 8 * 8), _fb(8)
+    ln = sm.sm_reduce_scatter_layernorm
+    assert _err(ln, p1, parts, out) == sm.SM_ERR_CASE
+    assert _err(ln, pk, _fb(4, 16 * 4), _fb(8)) == sm.SM_ERR_CASE  # K sharded: rows are not whole
+    assert _err(ln, p3, parts, out, None, None, -1.0) == sm.SM_ERR_ARG
+    q = sm.sm_plan({"X": 2}, "P(None, 'X')", "P('X', None)", 8, 8, 6)
+    assert _err(ln, q, _fb(8, 64), _fb(8)) == sm.SM_ERR_SHAPE  # row length 6 not a multiple of 4
+    rs = sm.sm_reshard
+    assert _err(rs, {"X": 2}, "A[I, J_X]", "A[I_X, J]", 8, 8, sm.SM_F32, _fb(8), _fb(8)) == sm.SM_ERR_ARG
+    assert _err(rs, {"X": 3}, "A[I, J_X]", "A[I_X, J]", 8, 9, sm.SM_F32, _fb(4, 32), _fb(12, 48)) \
+        == sm.SM_ERR_INDIVISIBLE
+    assert _err(rs, {"X": 2}, "A[I_X, J_X]", "P()", 8, 8, sm.SM_F32, _fb(8, 32), _fb(8)) == sm.SM_ERR_AXIS_REUSED
+    assert _err(rs, {"X": 2}, "A[I, J_X]", "P()", 8, 8, 7, _fb(8, 32), _fb(8)) == sm.SM_ERR_DTYPE

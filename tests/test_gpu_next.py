@@ -165,3 +165,103 @@ def test_fused_reduce_full_downproj():
             say("fused float rel err", err)
             assert err <= REL_TOL
         del Ad, Bd, fused
+
+
+# ------------------------------------------------------------------ f3
+
+LN_TOL_INT = 1e-5   # exact pre-norm sums; float32 mean / variance / scaling
+LN_TOL = REL_TOL
+
+
+@pytest.mark.parametrize("integer", [True, False], ids=["int", "float"])
+def test_sp_tail_reduce_scatter_layernorm(integer):
+    """ana-alekseeva.com 'Sequence parallelism': RS, per-token layer norm on
+    the owned rows, AG. Global output (AG in place) and stacked output then
+    sm_gather_shards must agree bit for bit."""
+    mesh, sa, sb, I, J, K = {"X": 2, "Y": 2}, "P('X', 'Y')", "P('Y', None)", 512, 2 * 192, 520
+    say("case: sp tail", "int" if integer else "float")
+    mk = (lambda s, seed: wl.random_ints(s, seed)) if integer else (lambda s, seed: wl.random_normal(s, seed))
+    A, B = mk((I, J), 801), mk((J, K), 802)
+    p = sm.sm_plan(mesh, sa, sb, I, J, K)
+    q = planner.plan(mesh, sa, sb, I, J, K)
+    Ad, Bd = to_dev(A), to_dev(B)
+    _, P = run_partials(p, Ad, Bd)
+    rng = np.random.default_rng(803)
+    gamma = rng.standard_normal(K).astype(np.float32)
+    beta = rng.standard_normal(K).astype(np.float32)
+    gd, bd = torch.from_numpy(gamma).to(DEV), torch.from_numpy(beta).to(DEV)
+    parts = [ref.unit_partial(q, A, B, u) for u in range(q.n_units)]
+    tol = LN_TOL_INT if integer else LN_TOL
+    for g_, b_ in ((None, None), (gd, bd)):
+        fo, out = guarded((I, K), torch.float32)
+        sm.sm_reduce_scatter_layernorm(p, sm.buf(P), sm.buf(out), g_, b_, 1e-5)
+        want = ref.sp_tail(q, parts, None if g_ is None else gamma, None if b_ is None else beta, 1e-5)
+        err = ref.rel_frobenius(out.cpu().numpy(), want)
+        say("sp tail rel err", err)
+        assert err <= tol
+        assert guard_intact(fo, out.numel())
+        st = torch.empty(q.n_groups * q.n_partials, q.c_local[0] // q.n_partials, K, device=DEV)
+        sm.sm_reduce_scatter_layernorm(p, sm.buf(P), sm.buf(st), g_, b_, 1e-5)
+        ag = torch.empty(I, K, device=DEV)
+        sm.sm_gather_shards(p, sm.SM_WHAT_C_SCATTERED, sm.buf(st), sm.buf(ag))
+        assert torch.equal(ag, out)
+
+
+def test_sp_tail_full_downproj():
+    w = wl.get("downproj")
+    say("case: sp tail full downproj")
+    A = wl.make_operand(w.operand("A"))
+    B = wl.make_operand(w.operand("B"))
+    I, J = A.shape
+    K = B.shape[1]
+    p = sm.sm_plan(dict(w.mesh), w.operand("A").spec, w.operand("B").spec, I, J, K)
+    q = planner.plan(dict(w.mesh), w.operand("A").spec, w.operand("B").spec, I, J, K)
+    _, P = run_partials(p, to_dev(A), to_dev(B))
+    out = torch.empty(I, K, device=DEV)
+    sm.sm_reduce_scatter_layernorm(p, sm.buf(P), sm.buf(out), None, None, 1e-5)
+    m = q.c_local[0]
+    for g in (0, 3):
+        rows = sample_rows(m, 4, 900 + g)
+        parts = [ref.unit_partial(q, A, B, g * 2 + y, rows=rows) for y in range(2)]
+        want = ref.layer_norm(ref.sum_ranked(parts))
+        got = out[[g * m + r for r in rows]].cpu().numpy()
+        assert ref.rel_frobenius(got, want) <= LN_TOL
+
+
+# ------------------------------------------------------------------ f4
+
+RESHARD = [
+    ({"X": 4}, "A[I, J_X]", "A[I_X, J]", 512, 768),       # all-to-all
+    ({"X": 2, "Y": 2}, "A[I_XY, J]", "A[I_X, J_Y]", 256, 512),
+    ({"X": 4}, "A[I_X, J]", "P()", 256, 264),             # all-gather to replicated
+    ({"X": 2, "Y": 3}, "A[I, J_X]", "A[I, J_Y]", 64, 48),  # blocks straddle blocks
+]
+
+
+@pytest.mark.parametrize("case", RESHARD, ids=lambda c: f"{c[1]}->{c[2]}")
+@pytest.mark.parametrize("dtype", [sm.SM_BF16, sm.SM_F32], ids=["bf16", "f32"])
+def test_reshard_bitexact(case, dtype):
+    mesh, frm, to, R, Cc = case
+    say("case: reshard", case, dtype)
+    X = wl.random_normal((R, Cc), 950 + R)
+    if dtype == sm.SM_F32:
+        X = X.float()
+    tdt = torch.bfloat16 if dtype == sm.SM_BF16 else torch.float32
+    src_blocks = ref.shard(ref.stored(X)[0], mesh, frm)
+    src = to_dev(torch.from_numpy(np.stack([src_blocks[b] for b in sorted(src_blocks)])).view(tdt)
+                 if dtype == sm.SM_BF16 else torch.from_numpy(np.stack([src_blocks[b] for b in sorted(src_blocks)])))
+    want = ref.reshard(src_blocks, mesh, frm, to, R, Cc)
+    nb = len(want)
+    br, bc = next(iter(want.values())).shape
+    full = torch.full((nb * br * bc + 256,), 7, dtype=tdt, device=DEV)
+    dst = full[:nb * br * bc].view(nb, br, bc)
+    sm.sm_reshard(mesh, frm, to, R, Cc, dtype, sm.buf(src), sm.buf(dst))
+    got = ref.stored(dst.cpu())[0]
+    for b in range(nb):
+        np.testing.assert_array_equal(got[b], want[b])
+    assert bool((full[nb * br * bc:] == 7).all())
+    # global source layout gives the same blocks
+    Xd = to_dev(X)
+    dst2 = torch.empty_like(dst)
+    sm.sm_reshard(mesh, frm, to, R, Cc, dtype, sm.buf(Xd, block_stride=0), sm.buf(dst2))
+    assert torch.equal(dst2, dst)

@@ -266,6 +266,50 @@ def test_mlp_chain_parts_and_commuting_split():
     assert not np.allclose(Z, z_unrounded, rtol=1e-9, atol=0)
 
 
+# ----------------------------------------------------- layer norm, reshard
+
+def test_layer_norm_hand_example_and_library():
+    """Hand-worked: x = [1, 2, 3, 4]: mean 2.5, biased var 1.25, so
+    y = (x - 2.5) / sqrt(1.25 + eps). Library: torch's float64 layer_norm."""
+    x = np.array([[1.0, 2.0, 3.0, 4.0]])
+    want = (x - 2.5) / np.sqrt(1.25 + 1e-5)
+    np.testing.assert_allclose(ref.layer_norm(x), want, rtol=1e-15, atol=1e-15)
+    rng = np.random.default_rng(120)
+    X = rng.standard_normal((7, 33)) * 3 + 1
+    g = rng.standard_normal(33)
+    b = rng.standard_normal(33)
+    t = torch.nn.functional.layer_norm(torch.from_numpy(X), (33,), torch.from_numpy(g), torch.from_numpy(b), 1e-5)
+    np.testing.assert_allclose(ref.layer_norm(X, g, b), t.numpy(), rtol=1e-12, atol=1e-12)
+    y = ref.layer_norm(X, eps=0.0)
+    np.testing.assert_allclose(y.mean(axis=1), 0.0, atol=1e-13)
+    np.testing.assert_allclose((y * y).mean(axis=1), 1.0, rtol=1e-13)
+
+
+def test_sp_tail_equals_allreduce_then_norm():
+    """ana-alekseeva.com 'Sequence parallelism': reduce-scatter, per-token
+    norm, all-gather gives what all-reduce then the per-token norm gives."""
+    A = _ints((16, 24), 130)
+    B = _ints((24, 12), 131)
+    p = planner.plan({"X": 2, "Y": 2}, "P('X', 'Y')", "P('Y', None)", 16, 24, 12)
+    parts = ref.partials(p, A, B)
+    np.testing.assert_allclose(ref.sp_tail(p, parts), ref.layer_norm(A @ B), rtol=1e-12, atol=1e-12)
+
+
+def test_reshard_alltoall_blocks():
+    """learntpu.dev ch05: AllToAll A[I, J_X] -> A[I_X, J] moves which
+    dimension is sharded; an all-gather to P() gives the whole array."""
+    X = np.arange(8 * 12, dtype=np.float64).reshape(8, 12)
+    mesh = {"X": 4}
+    cols = ref.shard(X, mesh, "A[I, J_X]")
+    assert all(b.shape == (8, 3) for b in cols.values())
+    rows = ref.reshard(cols, mesh, "A[I, J_X]", "A[I_X, J]", 8, 12)
+    assert all(b.shape == (2, 12) for b in rows.values())
+    for i in range(4):
+        np.testing.assert_array_equal(rows[i], X[2 * i:2 * i + 2])
+    whole = ref.reshard(rows, mesh, "A[I_X, J]", "P()", 8, 12)
+    np.testing.assert_array_equal(whole[0], X)
+
+
 # ------------------------------------------------------------- Freivalds
 
 def test_freivalds_detects_one_wrong_entry():
