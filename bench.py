@@ -10,8 +10,10 @@ J = 28672; the sharding sandbox default of learntpu.dev ch05):
      [1024,8192] of the finished C, one launch.
 Inputs are resident in HBM before the timed region. One JSON line on stdout.
 
-The HIP events that time each kernel are recorded on the stream the kernels
-are launched on. `--copy-calibration` runs a plain device copy of a known
+The timed region is the K steps between two synchronisations (wall clock,
+and HIP events on the stream the kernels run on). Each kernel's average
+launch duration is then measured on its own: K launches queued back to back
+between two HIP events on that stream. `--copy-calibration` runs a plain device copy of a known
 size (for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE counters).
 """
 from __future__ import annotations
@@ -62,8 +64,9 @@ def setup(workload: str):
 
 
 def cpu_baseline(ctx, rows: int):
-    """The oracle (fp64 naive loops) on a bounded sample: `rows` output rows
-    of unit 0's local product, timed on the host cores."""
+    """The oracle (fp64 naive loops) on a bounded sample of the same step:
+    the first `rows` output rows of the local products, taken unit by unit
+    (unit 0's rows first), timed on the host cores."""
     import numpy as np
 
     from oracle import planner, reference as ref
@@ -74,16 +77,57 @@ def cpu_baseline(ctx, rows: int):
     q = planner.plan(dict(w.mesh), w.operand(names[0]).spec, w.operand(names[1]).spec, ctx["I"], ctx["J"], ctx["K"])
     m, n = q.c_local
     k = q.a_local[1]
-    rows = min(rows, m)
-    sel = np.arange(rows)
+    rows = min(rows, m * q.n_units)
+    done, units = 0, 0
     t0 = time.perf_counter()
-    ref.unit_partial(q, ctx["A"], ctx["B"], 0, rows=sel)
+    while done < rows:
+        take = min(m, rows - done)
+        ref.unit_partial(q, ctx["A"], ctx["B"], units, rows=np.arange(take))
+        done += take
+        units += 1
     dt = time.perf_counter() - t0
     flops = 2.0 * rows * n * k
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(load_library().orc_num_threads()),
             "kind": "oracle",
-            "sample": f"{rows} output rows of unit 0's local product [{m},{k}]x[{k},{n}] "
+            "sample": f"{rows} output rows of the local products [{m},{k}]x[{k},{n}] of units 0..{units - 1} "
                       f"({flops / 1e9:.1f} GFLOP, fp64 naive loops, {dt:.1f} s)"}
+
+
+def source_digest(paths) -> str:
+    """sha256 over the listed source files (repository-relative), in order."""
+    import hashlib
+
+    h = hashlib.sha256()
+    for rel in paths:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def recorded_traffic(launch: str, workload: str):
+    """HBM bytes per launch measured by rocprofv3 counters (FETCH_SIZE and
+    WRITE_SIZE, scaled by a plain-copy calibration), as recorded in a
+    `traffic-record:` line of a counter summary under profiles/. Returns None
+    when there is no record for this launch ("gemm", "reduce" or "fused") and
+    workload, or when the kernel's sources changed after the counters were
+    taken."""
+    import glob
+
+    for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "*.md"))):
+        with open(path) as f:
+            for line in f:
+                if not line.startswith("traffic-record:"):
+                    continue
+                kv = dict(tok.split("=", 1) for tok in line.split()[1:] if "=" in tok)
+                if kv.get("launch") != launch or kv.get("workload") != workload:
+                    continue
+                try:
+                    if source_digest(kv["sources"].split("+")) != kv.get("sha256"):
+                        return None
+                except OSError:
+                    return None
+                return float(kv["bytes"])
+    return None
 
 
 def copy_calibration(mib: int, reps: int) -> None:
@@ -104,7 +148,7 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="downproj")
-    ap.add_argument("--cpu-rows", type=int, default=768, help="oracle sample size (rows of unit 0)")
+    ap.add_argument("--cpu-rows", type=int, default=6144, help="oracle sample size (output rows, unit by unit)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB")
     args = ap.parse_args()
@@ -127,38 +171,57 @@ def main() -> int:
     a, b, c, o = sm.buf(ctx["Ad"]), sm.buf(ctx["Bd"]), sm.buf(P), sm.buf(out)
     stream = torch.cuda.current_stream()
 
-    def step(evs=None):
-        if evs:
-            evs[0].record(stream)
+    def gemm():
         sm.sm_local_gemm(p, a, b, c, sm.SM_EPI_STORE, 0, p.n_units, stream)
-        if evs:
-            evs[1].record(stream)
+
+    def reduce():
+        sm.sm_reduce_partials(p, c, o, mode, 0, p.n_groups, stream)
+
+    def fused_call():
+        sm.sm_local_gemm_reduce(p, a, b, o, mode, 0, p.n_groups, stream)
+
+    def step():
+        gemm()
         if p.kase == sm.SM_CASE3:
-            sm.sm_reduce_partials(p, c, o, mode, 0, p.n_groups, stream)
-        if evs:
-            evs[2].record(stream)
+            reduce()
+
+    def back_to_back(fn, reps):
+        """Average duration of one launch: `reps` launches queued back to back
+        on the kernels' stream between two HIP events."""
+        fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
 
     log(f"bench: warmup {args.warmup}")
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     log(f"bench: timing {args.steps} steps")
+    s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for k in range(args.steps):
-        step(evs[k])
+    s0.record(stream)
+    for _ in range(args.steps):
+        step()
+    s1.record(stream)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_step = (t1 - t0) * 1e3 / args.steps
-    gemm_ms = sorted(e[0].elapsed_time(e[1]) for e in evs)
-    red_ms = sorted(e[1].elapsed_time(e[2]) for e in evs)
-    gemm_avg = sum(gemm_ms) / len(gemm_ms)
-    red_avg = sum(red_ms) / len(red_ms)
+    ms_step_events = s0.elapsed_time(s1) / args.steps
+
+    # Per-kernel launch durations, each kernel on its own.
+    gemm_avg = back_to_back(gemm, args.steps)
+    red_avg = back_to_back(reduce, args.steps) if p.kase == sm.SM_CASE3 else 0.0
 
     m, n = p.c_local[0], p.c_local[1]
-    k = p.a_local[1]
-    gemm_flops = 2.0 * m * n * k * p.n_units
+    kl = p.a_local[1]
+    gemm_flops = 2.0 * m * n * kl * p.n_units
     N = p.n_partials
     # reduce: each group reads N fp32 partials and writes one fp32 block
     red_bytes = (N + 1) * m * n * 4.0 * p.n_groups if p.kase == sm.SM_CASE3 else 0.0
@@ -176,26 +239,20 @@ def main() -> int:
     # launch, no partial buffers) on the same inputs, timed the same way.
     fused = None
     if p.kase == sm.SM_CASE3 and m > 16:
-        fev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
-        for _ in range(2):
-            sm.sm_local_gemm_reduce(p, a, b, o, mode, 0, p.n_groups, stream)
-        torch.cuda.synchronize()
-        for k in range(args.steps):
-            fev[k][0].record(stream)
-            sm.sm_local_gemm_reduce(p, a, b, o, mode, 0, p.n_groups, stream)
-            fev[k][1].record(stream)
-        torch.cuda.synchronize()
-        f_ms = sorted(e[0].elapsed_time(e[1]) for e in fev)
-        f_avg = sum(f_ms) / len(f_ms)
-        fused = {"avg_ms": round(f_avg, 4), "min_ms": round(f_ms[0], 4),
+        f_avg = back_to_back(fused_call, args.steps)
+        fused = {"avg_ms": round(f_avg, 4),
                  "tflops": round(gemm_flops / (f_avg * 1e-3) / 1e12, 1),
-                 "vs_gemm_plus_reduce": round((gemm_avg + red_avg) / f_avg, 3)}
+                 "vs_gemm_plus_reduce": round((gemm_avg + red_avg) / f_avg, 3),
+                 "traffic": recorded_traffic("fused", ctx["w"].name)}
 
     cpu = None
     if not args.no_cpu_baseline:
         log(f"bench: oracle CPU baseline on {args.cpu_rows} rows")
         cpu = cpu_baseline(ctx, args.cpu_rows)
 
+    # HBM bytes per launch from rocprofv3 counters (null when not recorded for
+    # the kernel as it is now)
+    gemm_traffic = recorded_traffic("gemm", ctx["w"].name)
     line = {
         "metric": METRIC,
         "value": round(gemm_flops / (ms_step * 1e-3) / 1e12, 2),
@@ -214,21 +271,23 @@ def main() -> int:
             "mesh": "{X:4,Y:2}" if args.workload == "downproj" else str(dict(ctx["w"].mesh)),
             "global": f"A[{ctx['I']},{ctx['J']}] . B[{ctx['J']},{ctx['K']}]",
             "units": int(p.n_units),
-            "local_gemm": f"[{m},{k}]x[{k},{n}] bf16 -> fp32",
+            "local_gemm": f"[{m},{kl}]x[{kl},{n}] bf16 -> fp32",
             "reduce": ("reduce-scatter" if mode == sm.SM_REDUCESCATTER else "all-reduce")
                       + f" {p.n_groups} groups x {N} fp32 partials [{m},{n}]",
         },
-        "gemm": {"avg_ms": round(gemm_avg, 4), "min_ms": round(gemm_ms[0], 4),
+        "ms_per_step_events": round(ms_step_events, 4),
+        "gemm": {"avg_ms": round(gemm_avg, 4),
                  "tflops": round(gemm_tflops, 1), "frac_of_peak": round(gemm_tflops / PEAK_BF16_TFLOPS, 4),
                  "bytes": gemm_bytes, "gbps": round(gemm_gbps, 1)},
-        "reduce": {"avg_ms": round(red_avg, 4), "min_ms": round(red_ms[0], 4), "bytes": red_bytes,
+        "reduce": {"avg_ms": round(red_avg, 4), "bytes": red_bytes,
                    "gbps": round(red_gbps, 1), "frac_of_peak": round(red_gbps / PEAK_HBM_GBPS, 4)},
         "roofline": ({"bound": "hbm", "achieved": round(gemm_gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                      "frac": round(gemm_gbps / PEAK_HBM_GBPS, 4), "traffic": None} if skinny else
+                      "frac": round(gemm_gbps / PEAK_HBM_GBPS, 4), "traffic": gemm_traffic} if skinny else
                      {"bound": "mfma", "achieved": round(gemm_tflops, 1), "peak": PEAK_BF16_TFLOPS,
-                      "unit": "TFLOP/s", "frac": round(gemm_tflops / PEAK_BF16_TFLOPS, 4), "traffic": None}),
+                      "unit": "TFLOP/s", "frac": round(gemm_tflops / PEAK_BF16_TFLOPS, 4), "traffic": gemm_traffic}),
         "roofline_reduce": {"bound": "hbm", "achieved": round(red_gbps, 1), "peak": PEAK_HBM_GBPS,
-                            "unit": "GB/s", "frac": round(red_gbps / PEAK_HBM_GBPS, 4), "traffic": None},
+                            "unit": "GB/s", "frac": round(red_gbps / PEAK_HBM_GBPS, 4),
+                            "traffic": recorded_traffic("reduce", ctx["w"].name)},
         "fused_gemm_reduce": fused,
         "cpu_baseline": cpu,
         "context": "learntpu.dev sandbox, modelled (not measured) on Ironwood: 481 GFLOP local matmul "
