@@ -5,18 +5,23 @@
 // have the full output shape and are summed afterwards).
 //
 // Design (gfx950): the work is bound by HBM reads of A_u, so the kernel is
-// shaped for bytes in flight, not for matrix-core throughput.
-//  * One workgroup = 8 waves = one unit and 128 output columns; the unit's
-//    K range is split into 8 contiguous slices, one per wave.
-//  * A wave walks its slice 32 rows at a time. Lane (g = lane/16, j =
-//    lane%16) loads the 8x8 block rows k0+8g..+8, columns n0+8j..+8 of A_u
-//    (16 lanes read 256 contiguous bytes of a row), transposes it in
-//    registers, and issues 8 v_mfma_f32_16x16x32_bf16: MFMA c covers the
-//    strided column set {n0 + 8j + c : j = 0..15}. X_u's fragment (row
-//    lane%16, 8 consecutive k) is a 16-byte load that stays in L2.
-//  * The next step's 8 loads are in flight while a step's MFMAs run; at
-//    most 128 VGPRs, so two workgroups (16 waves) share a CU.
-//  * The 8 wave partials are added in LDS in wave order (a fixed order, so
+// shaped for the access pattern HBM streams best, not for matrix-core
+// throughput (measured on the [28672, 8192] bf16 stream: workgroups that own
+// 256 columns and read 512 contiguous bytes per row per 32 lanes reach
+// 6.4-6.6 TB/s; 128-column workgroups stay at 5.9 TB/s).
+//  * One workgroup = 4 waves = one unit and 256 output columns; the unit's
+//    K range is split into 4 contiguous slices, one per wave.
+//  * A wave walks its slice 16 rows at a time. Lane (h = lane/32, j =
+//    lane%32) loads the 8x8 block rows k0+8h..+8, columns n0+8j..+8 of A_u
+//    (32 lanes read 512 contiguous bytes of a row), transposes it in
+//    registers, and issues 8 v_mfma_f32_32x32x16_bf16. Their B operand is
+//    exactly that layout (lane l: column l%32, k-group l/32): MFMA c covers
+//    the strided column set {n0 + 8j + c : j = 0..31}. X_u's fragment (row
+//    lane%32, 8 consecutive k) is a 16-byte load that stays in L2; rows
+//    M..31 of the MFMA are zero, so half of the matrix-core work is padding
+//    on a path that keeps the matrix cores under 10 % busy.
+//  * The next step's 8 loads are in flight while a step's MFMAs run.
+//  * The 4 wave partials are added in LDS in wave order (a fixed order, so
 //    the result is deterministic) and stored once.
 #include "kernels.h"
 
@@ -24,19 +29,20 @@ namespace shardmm {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int WAVES = 8;
+constexpr int WAVES = 4;
 constexpr int NT = 64 * WAVES;
-constexpr int COLS = 128;  // output columns per workgroup
-constexpr int KSTEP = 32;  // rows of A per MFMA step
+constexpr int COLS = 256;  // output columns per workgroup
+constexpr int KSTEP = 16;  // rows of A per MFMA step
+constexpr int MROWS = 16;  // output rows kept (M <= 16)
 
 __device__ __forceinline__ uint4 load16(const uint16_t* p) {
   return *reinterpret_cast<const uint4*>(p);
 }
 
-// A_u is read exactly once: non-temporal loads (measured on this access
-// pattern: 5.4 -> 6.2 TB/s).
+// A_u is read exactly once: non-temporal loads (plain loads of the same
+// stream run at about half the rate).
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ uint4 load16_stream(const uint16_t* p) {
   const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
@@ -95,9 +101,9 @@ struct StepRegs {
 
 template <bool EDGE>
 __device__ __forceinline__ void load_step(StepRegs& r, const uint16_t* X, int64_t ldx, const uint16_t* A,
-                                          int64_t lda, int M, int K, int N, int k0, int n0, int g, int j,
+                                          int64_t lda, int M, int K, int N, int k0, int n0, int h, int j,
                                           bool vec) {
-  const int kx = k0 + 8 * g;
+  const int kx = k0 + 8 * h;
   if (EDGE || j >= M)
     r.x = load16_guarded(X, ldx, j, kx, M, K, vec);
   else
@@ -112,46 +118,49 @@ __device__ __forceinline__ void load_step(StepRegs& r, const uint16_t* X, int64_
 }
 
 template <bool EDGE, bool OUT_BF16, bool GELU>
-__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4, 4))) void gemm_skinny_kernel(const GemmLaunch L) {
-  __shared__ float red[WAVES][16][COLS];
+__global__ __launch_bounds__(NT) void gemm_skinny_kernel(const GemmLaunch L) {
+  __shared__ float red[WAVES][MROWS][COLS];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int g = lane >> 4, j = lane & 15;
+  const int h = lane >> 5, j = lane & 31;
   const int n0 = blockIdx.x * COLS;
   const GemmUnitPtrs U = L.u[blockIdx.y];
   const int M = L.M, N = L.N, K = L.K;
 
-  // This wave's slice of whole 32-row steps.
+  // This wave's slice of whole 16-row steps.
   const int steps = (K + KSTEP - 1) / KSTEP;
   const int s_begin = (steps * wave) / WAVES;
   const int s_end = (steps * (wave + 1)) / WAVES;
 
-  f32x4 acc[8];
+  f32x16 acc[8];
 #pragma unroll
-  for (int c = 0; c < 8; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int c = 0; c < 8; ++c)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) acc[c][v] = 0.f;
 
   // One set of load registers: once a step's block has been transposed into
   // the MFMA operands, the load registers take the next step's loads while
   // the 8 MFMAs run.
   StepRegs r;
-  if (s_begin < s_end) load_step<EDGE>(r, U.a, L.lda, U.b, L.ldb, M, K, N, s_begin * KSTEP, n0, g, j, L.vec_ok);
+  if (s_begin < s_end) load_step<EDGE>(r, U.a, L.lda, U.b, L.ldb, M, K, N, s_begin * KSTEP, n0, h, j, L.vec_ok);
   for (int s = s_begin; s < s_end; ++s) {
     uint4 t[8];
     transpose8(r.a, t);
     const bf16x8 xf = __builtin_bit_cast(bf16x8, r.x);
-    if (s + 1 < s_end) load_step<EDGE>(r, U.a, L.lda, U.b, L.ldb, M, K, N, (s + 1) * KSTEP, n0, g, j, L.vec_ok);
+    if (s + 1 < s_end) load_step<EDGE>(r, U.a, L.lda, U.b, L.ldb, M, K, N, (s + 1) * KSTEP, n0, h, j, L.vec_ok);
 #pragma unroll
     for (int c = 0; c < 8; ++c)
-      acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xf, __builtin_bit_cast(bf16x8, t[c]), acc[c], 0, 0, 0);
+      acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xf, __builtin_bit_cast(bf16x8, t[c]), acc[c], 0, 0, 0);
   }
 
-  // Output of MFMA c, register v: row 4g + v, column n0 + 8j + c.
+  // Output of MFMA c, register v: row 8(v/4) + 4h + v%4, column n0 + 8j + c.
+  // Registers 0..7 hold rows 0..15; registers 8..15 hold the zero rows.
 #pragma unroll
   for (int c = 0; c < 8; ++c)
 #pragma unroll
-    for (int v = 0; v < 4; ++v) red[wave][4 * g + v][8 * j + c] = acc[c][v];
+    for (int v = 0; v < 8; ++v) red[wave][8 * (v >> 2) + 4 * h + (v & 3)][8 * j + c] = acc[c][v];
   __syncthreads();
 
-  for (int o = tid; o < 16 * COLS; o += NT) {
+  for (int o = tid; o < MROWS * COLS; o += NT) {
     const int m = o / COLS, col = o % COLS;
     float sum = red[0][m][col];
 #pragma unroll

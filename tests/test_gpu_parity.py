@@ -141,6 +141,8 @@ SKINNY = [
     ({"T": 8}, "P(None, 'T')", "P('T', None)", 16, 8 * 256, 1024),  # full tiles
     ({"T": 2}, "P(None, 'T')", "P('T', None)", 1, 2 * 64, 136),     # one row
     ({"X": 2}, "P()", "P(None, 'X')", 16, 96, 2 * 128),              # case 1, skinny
+    ({"T": 2}, "P(None, 'T')", "P('T', None)", 16, 2 * 112, 768),   # 7 K steps over 4 waves, 3 column blocks
+    ({"T": 2}, "P(None, 'T')", "P('T', None)", 3, 2 * 16, 512),     # one K step: three waves idle
 ]
 
 
@@ -157,6 +159,27 @@ def test_skinny_shapes_bitexact(case):
     for u in range(q.n_units):
         assert f32_bits_equal(Pn[u], ref.unit_partial(q, A, B, u)), u
     assert guard_intact(full, P.numel())
+
+
+@pytest.mark.parametrize("width", [256, 288], ids=["interior", "ragged"])
+def test_gelu_epilogue_skinny(width):
+    """The GeLU(tanh) -> bfloat16 epilogue on the skinny path (M <= 16):
+    column blocks of a small batch, within the derived bound of the oracle's
+    round_bf16(gelu(.))."""
+    say("case: gelu epilogue skinny", width)
+    F = 4 * width
+    X = wl.random_normal((12, 160), 34)
+    W1 = wl.random_normal((160, F), 35, 0.1)
+    W2 = wl.random_normal((F, 64), 36, 0.1)
+    p1, q1 = _plans({"T": 4}, "P(None, None)", "P(None, 'T')", 12, 160, F, sm.SM_BF16)
+    _, q2 = _plans({"T": 4}, "P(None, 'T')", "P('T', None)", 12, F, 64)
+    H = torch.empty(12, F, dtype=torch.bfloat16, device=DEV)
+    sm.sm_local_gemm(p1, sm.buf(to_dev(X)), sm.buf(to_dev(W1)), sm.buf(H), sm.SM_EPI_GELU_TANH)
+    Hw, _ = ref.mlp_chain(q1, q2, X, W1, W2)
+    Hg = H.cpu().view(torch.int16).numpy().view(np.uint16)
+    absdot = ref.matmul(np.abs(ref.widen(X)), np.abs(ref.widen(W1)))
+    assert gelu_h_within_bound(Hg, Hw, absdot, 160).all()
+    assert (Hg != Hw).mean() < 0.01
 
 
 def test_gelu_epilogue_small():
