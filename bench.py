@@ -93,6 +93,115 @@ def cpu_baseline(ctx, rows: int):
                       f"({flops / 1e9:.1f} GFLOP, fp64 naive loops, {dt:.1f} s)"}
 
 
+def rate(bound: str, work: float, ms: float) -> dict:
+    """Roofline entry for one launch: `work` is flops (bound "mfma") or
+    bytes (bound "hbm") per launch, `ms` its average duration."""
+    if bound == "mfma":
+        achieved, peak, unit = work / (ms * 1e-3) / 1e12, PEAK_BF16_TFLOPS, "TFLOP/s"
+    else:
+        achieved, peak, unit = work / (ms * 1e-3) / 1e9, PEAK_HBM_GBPS, "GB/s"
+    return {"avg_ms": round(ms, 4), "bound": bound, "achieved": round(achieved, 1), "peak": peak, "unit": unit,
+            "frac": round(achieved / peak, 4), "work": work}
+
+
+def measure_rows(back_to_back, stream) -> dict:
+    """The other rows of the path on their own workloads, each launch timed
+    back to back like the step's kernels:
+      a4  Megatron MLP chain [4096,4096] . W1[4096,16384] (4 column blocks,
+          GeLU(tanh) -> bf16 epilogue) . W2[16384,4096] (4 row blocks), then
+          the all-reduce of the 4 fp32 partials;
+      a6  case 1 on {X:4,Y:2} at 4096^3: 8 local blocks, then the gather of
+          the 8 fp32 blocks into the global C;
+      f1  case 2 A[I,J_X] . B[J,K] at 4096^3: all-gather A, then the case-1
+          product of the gathered plan;
+      f3  the sequence-parallel tail on the MLP's 4 partials: reduce-scatter,
+          per-token layer norm (with gamma, beta), all-gather;
+      f4  the all-to-all reshard A[I,J_X] -> A[I_X,J] of a bf16 [4096,4096]."""
+    import torch
+
+    import local_shard_gemm_amd as sm
+    import workloads as wl
+
+    dev = torch.device("cuda:0")
+    rows = {}
+
+    # a4 (+ f3 on the same partials)
+    w = wl.get("mlp")
+    X = wl.make_operand(w.operand("X")).to(dev)
+    W1 = wl.make_operand(w.operand("W1")).to(dev)
+    W2 = wl.make_operand(w.operand("W2")).to(dev)
+    B_, D = X.shape
+    F = W1.shape[1]
+    p1 = sm.sm_plan(dict(w.mesh), w.operand("X").spec, w.operand("W1").spec, B_, D, F, out_dtype=sm.SM_BF16)
+    p2 = sm.sm_plan(dict(w.mesh), "P(None, 'T')", w.operand("W2").spec, B_, F, D)
+    H = torch.empty(B_, F, dtype=torch.bfloat16, device=dev)
+    P = torch.empty(p2.n_units, B_, D, dtype=torch.float32, device=dev)
+    Z = torch.empty(B_, D, dtype=torch.float32, device=dev)
+    bx, bw1, bw2, bh, bp, bz = (sm.buf(t) for t in (X, W1, W2, H, P, Z))
+    l1 = back_to_back(lambda: sm.sm_local_gemm(p1, bx, bw1, bh, sm.SM_EPI_GELU_TANH, 0, p1.n_units, stream))
+    l2 = back_to_back(lambda: sm.sm_local_gemm(p2, bh, bw2, bp, sm.SM_EPI_STORE, 0, p2.n_units, stream))
+    ar = back_to_back(lambda: sm.sm_reduce_partials(p2, bp, bz, sm.SM_ALLREDUCE, 0, p2.n_groups, stream))
+    layer_flops = 2.0 * B_ * D * F
+    rows["a4_mlp_chain"] = {
+        "workload": w.name,
+        "layer1_gemm_gelu_bf16": rate("mfma", layer_flops, l1),
+        "layer2_gemm": rate("mfma", layer_flops, l2),
+        "allreduce": rate("hbm", (p2.n_partials + 1) * B_ * D * 4.0, ar),
+        "chain_ms": round(l1 + l2 + ar, 4),
+    }
+    g = torch.randn(D, device=dev)
+    bta = torch.randn(D, device=dev)
+    sp = back_to_back(lambda: sm.sm_reduce_scatter_layernorm(p2, bp, bz, g, bta, 1e-5, 0, p2.n_groups, stream))
+    rows["f3_sp_tail"] = {"workload": w.name + ": reduce-scatter 4 x [4096,4096] -> layer norm -> all-gather",
+                          **rate("hbm", (p2.n_partials + 1) * B_ * D * 4.0 + 2 * D * 4.0, sp)}
+    del X, W1, W2, H, P, Z, bx, bw1, bw2, bh, bp, bz
+
+    # a6
+    w = wl.get("case1")
+    A = wl.make_operand(w.operand("A")).to(dev)
+    Bm = wl.make_operand(w.operand("B")).to(dev)
+    I, J = A.shape
+    K = Bm.shape[1]
+    p = sm.sm_plan(dict(w.mesh), w.operand("A").spec, w.operand("B").spec, I, J, K)
+    m, n = p.c_local
+    Pc = torch.empty(p.n_units, m, n, dtype=torch.float32, device=dev)
+    C = torch.empty(I, K, dtype=torch.float32, device=dev)
+    ba, bb, bpc, bc = sm.buf(A), sm.buf(Bm), sm.buf(Pc), sm.buf(C)
+    gm = back_to_back(lambda: sm.sm_local_gemm(p, ba, bb, bpc, sm.SM_EPI_STORE, 0, p.n_units, stream))
+    ga = back_to_back(lambda: sm.sm_gather_shards(p, sm.SM_WHAT_C_BLOCKS, bpc, bc, stream))
+    rows["a6_case1_gather"] = {"workload": w.name,
+                               "gemm": rate("mfma", 2.0 * m * n * p.a_local[1] * p.n_units, gm),
+                               "gather": rate("hbm", 2 * 4.0 * I * K, ga)}
+
+    # f1: case 2 at the same sizes, A held as 4 column blocks
+    mesh = {"X": 4, "Y": 2}
+    p = sm.sm_plan(mesh, "A[I, J_X]", "B[J, K]", I, J, K)
+    gr, gc = p.a_grid
+    blocks = torch.stack([A[i * (I // gr):(i + 1) * (I // gr), j * (J // gc):(j + 1) * (J // gc)]
+                          for i in range(gr) for j in range(gc)]).contiguous()
+    Ag = torch.empty(I, J, dtype=torch.bfloat16, device=dev)
+    p_g = sm.sm_plan_gathered(p)
+    Cg = torch.empty(p_g.n_units, p_g.c_local[0], p_g.c_local[1], dtype=torch.float32, device=dev)
+    bbl, bag, bcg = sm.buf(blocks), sm.buf(Ag), sm.buf(Cg)
+    gA = back_to_back(lambda: sm.sm_gather_shards(p, sm.SM_WHAT_A, bbl, bag, stream))
+    gg = back_to_back(lambda: sm.sm_local_gemm(p_g, bag, bb, bcg, sm.SM_EPI_STORE, 0, p_g.n_units, stream))
+    rows["f1_case2_gather_then_gemm"] = {
+        "workload": f"A[I,J_X] . B[J,K] on {{X:4,Y:2}}, I = J = K = {I}",
+        "gather_A": rate("hbm", 2 * 2.0 * I * J, gA),
+        "gemm": rate("mfma", 2.0 * p_g.c_local[0] * p_g.c_local[1] * p_g.a_local[1] * p_g.n_units, gg)}
+
+    # f4: all-to-all reshard of A's column blocks into row blocks
+    dst = torch.empty(4, I // 4, J, dtype=torch.bfloat16, device=dev)
+    mesh4 = sm.sm_mesh_init({"X": 4})
+    frm, to = sm.sm_parse_spec(mesh4, "A[I, J_X]"), sm.sm_parse_spec(mesh4, "A[I_X, J]")
+    blocks4 = torch.stack([A[:, j * (J // 4):(j + 1) * (J // 4)] for j in range(4)]).contiguous()
+    b4, bd4 = sm.buf(blocks4), sm.buf(dst)
+    rs = back_to_back(lambda: sm.sm_reshard(mesh4, frm, to, I, J, sm.SM_BF16, b4, bd4, stream))
+    rows["f4_alltoall_reshard"] = {"workload": f"bf16 [{I},{J}] A[I,J_X] -> A[I_X,J] on {{X:4}}",
+                                   **rate("hbm", 2 * 2.0 * I * J, rs)}
+    return rows
+
+
 def source_digest(paths) -> str:
     """sha256 over the listed source files (repository-relative), in order."""
     import hashlib
@@ -150,6 +259,7 @@ def main() -> int:
     ap.add_argument("--workload", default="downproj")
     ap.add_argument("--cpu-rows", type=int, default=6144, help="oracle sample size (output rows, unit by unit)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-rows", action="store_true", help="skip the measurements of the other rows")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB")
     args = ap.parse_args()
 
@@ -187,10 +297,14 @@ def main() -> int:
 
     def back_to_back(fn, reps):
         """Average duration of one launch: `reps` launches queued back to back
-        on the kernels' stream between two HIP events."""
+        on the kernels' stream between two HIP events. A ~5 ms spin kernel
+        goes first, so that all launches are queued before the GPU reaches
+        them and host-side call overhead never shows between short kernels."""
         fn()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
+        with torch.cuda.stream(stream):
+            torch.cuda._sleep(10_000_000)
         e0.record(stream)
         for _ in range(reps):
             fn()
@@ -245,6 +359,11 @@ def main() -> int:
                  "vs_gemm_plus_reduce": round((gemm_avg + red_avg) / f_avg, 3),
                  "traffic": recorded_traffic("fused", ctx["w"].name)}
 
+    rows = None
+    if not args.no_rows:
+        log("bench: the other rows of the path")
+        rows = measure_rows(lambda fn: back_to_back(fn, args.steps), stream)
+
     cpu = None
     if not args.no_cpu_baseline:
         log(f"bench: oracle CPU baseline on {args.cpu_rows} rows")
@@ -289,6 +408,7 @@ def main() -> int:
                             "unit": "GB/s", "frac": round(red_gbps / PEAK_HBM_GBPS, 4),
                             "traffic": recorded_traffic("reduce", ctx["w"].name)},
         "fused_gemm_reduce": fused,
+        "rows": rows,
         "cpu_baseline": cpu,
         "context": "learntpu.dev sandbox, modelled (not measured) on Ironwood: 481 GFLOP local matmul "
                    "in 209 us per rank",

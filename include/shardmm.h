@@ -32,8 +32,11 @@
  *  - Matrices are row-major. An sm_buf describes one buffer: base pointer,
  *    leading dimension ld (elements between consecutive rows), block_stride
  *    (elements between consecutive blocks of a stacked layout, or 0 for the
- *    global layout) and elems (number of elements the buffer holds; every
- *    access is checked against it on the host).
+ *    global layout), elems (number of elements the buffer holds; every
+ *    access is checked against it on the host) and dtype (SM_BF16 or
+ *    SM_F32, the type of those elements). A call that reads or writes a
+ *    buffer as another element type than its dtype fails with SM_ERR_DTYPE,
+ *    so element counts are never applied to the wrong element size.
  *  - Alignment: base pointers 16-byte aligned; ld and block_stride multiples
  *    of 8 elements for bfloat16 and of 4 for float32 (SM_ERR_ALIGN).
  */
@@ -47,7 +50,7 @@
 extern "C" {
 #endif
 
-#define SM_ABI_VERSION 1
+#define SM_ABI_VERSION 2
 #define SM_MAX_AXES 4
 #define SM_NAME_LEN 8
 
@@ -143,6 +146,8 @@ typedef struct {
   int64_t ld;
   int64_t block_stride;
   int64_t elems;
+  int32_t dtype;     /* sm_dtype of the elements */
+  int32_t reserved;  /* set to 0 */
 } sm_buf;
 
 /* ABI version and the size of sm_plan_t, for bindings to check layouts. */

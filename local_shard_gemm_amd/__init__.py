@@ -23,7 +23,7 @@ LIB_PATH = os.path.join(HERE, "libshardmm.so")
 
 SM_MAX_AXES = 4
 SM_NAME_LEN = 8
-SM_ABI_VERSION = 1
+SM_ABI_VERSION = 2
 
 # sm_status
 SM_OK = 0
@@ -101,7 +101,8 @@ class sm_rank_info_t(ctypes.Structure):
 
 class sm_buf(ctypes.Structure):
     _fields_ = [("ptr", ctypes.c_void_p), ("ld", ctypes.c_int64),
-                ("block_stride", ctypes.c_int64), ("elems", ctypes.c_int64)]
+                ("block_stride", ctypes.c_int64), ("elems", ctypes.c_int64),
+                ("dtype", ctypes.c_int32), ("reserved", ctypes.c_int32)]
 
 
 class ShardmmError(RuntimeError):
@@ -218,6 +219,16 @@ def sm_rank_info(plan: sm_plan_t, rank: int) -> sm_rank_info_t:
     return r
 
 
+def _dtype_of(t) -> int:
+    import torch
+
+    if t.dtype == torch.bfloat16:
+        return SM_BF16
+    if t.dtype == torch.float32:
+        return SM_F32
+    raise ValueError(f"buffers hold bfloat16 or float32 elements, not {t.dtype}")
+
+
 def buf(t, ld: Optional[int] = None, block_stride: Optional[int] = None) -> sm_buf:
     """sm_buf for a contiguous tensor: 2-D [rows, ld] = global layout
     (block_stride 0), 3-D [blocks, rows, ld] = stacked layout."""
@@ -227,7 +238,7 @@ def buf(t, ld: Optional[int] = None, block_stride: Optional[int] = None) -> sm_b
         ld = t.shape[-1]
     if block_stride is None:
         block_stride = t.shape[-2] * t.shape[-1] if t.dim() == 3 else 0
-    b = sm_buf(ctypes.c_void_p(t.data_ptr()), int(ld), int(block_stride), int(t.numel()))
+    b = sm_buf(ctypes.c_void_p(t.data_ptr()), int(ld), int(block_stride), int(t.numel()), _dtype_of(t), 0)
     b._tensor = t  # keep the memory alive as long as the descriptor
     return b
 

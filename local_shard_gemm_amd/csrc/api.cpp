@@ -14,9 +14,14 @@
 
 namespace shardmm {
 
+static const char* dtype_name(int32_t d) { return d == SM_BF16 ? "bfloat16" : d == SM_F32 ? "float32" : "unknown"; }
+
 int32_t check_buf_basic(const sm_buf* b, const char* what, int32_t dtype) {
   if (!b) return fail(SM_ERR_ARG, std::string(what) + ": NULL sm_buf");
   if (!b->ptr) return fail(SM_ERR_ARG, std::string(what) + ": NULL pointer");
+  if (b->dtype != dtype)
+    return fail(SM_ERR_DTYPE, std::string(what) + ": buffer holds " + dtype_name(b->dtype) + " elements, the call " +
+                                  "accesses it as " + dtype_name(dtype));
   if (reinterpret_cast<uintptr_t>(b->ptr) % 16)
     return fail(SM_ERR_ALIGN, std::string(what) + ": pointer not 16-byte aligned");
   const int64_t q = dtype == SM_BF16 ? 8 : 4;

@@ -222,8 +222,11 @@ def test_plan_dtype_rules():
 FAKE = 0x10000  # never dereferenced: every call below fails validation first
 
 
-def _fb(ld, stride=0, elems=1 << 40, ptr=FAKE):
-    return sm.sm_buf(ctypes.c_void_p(ptr), ld, stride, elems)
+BF, F32 = sm.SM_BF16, sm.SM_F32
+
+
+def _fb(ld, stride=0, elems=1 << 40, ptr=FAKE, dt=F32):
+    return sm.sm_buf(ctypes.c_void_p(ptr), ld, stride, elems, dt, 0)
 
 
 def _err(fn, *args):
@@ -237,7 +240,7 @@ def test_local_gemm_validation():
     p2 = sm.sm_plan({"X": 2}, "P(None, 'X')", "P()", 64, 128, 64)
     p4 = sm.sm_plan({"X": 2}, "P('X', None)", "P(None, 'X')", 64, 128, 64)
     p1 = sm.sm_plan({"X": 2}, "P('X', None)", "P()", 64, 128, 64)
-    A, B = _fb(128), _fb(64)
+    A, B = _fb(128, dt=BF), _fb(64, dt=BF)
     Cs = _fb(64, 64 * 64)
     assert _err(sm.sm_local_gemm, p2, A, B, Cs) == sm.SM_ERR_NEEDS_GATHER
     assert _err(sm.sm_local_gemm, p4, A, B, Cs) == sm.SM_ERR_NEEDS_GATHER
@@ -245,10 +248,10 @@ def test_local_gemm_validation():
     assert _err(sm.sm_local_gemm, p3, A, B, Cs, sm.SM_EPI_GELU_TANH) == sm.SM_ERR_CASE
     assert _err(sm.sm_local_gemm, p3, A, B, Cs, 7) == sm.SM_ERR_ARG
     assert _err(sm.sm_local_gemm, p3, A, B, Cs, 0, 1, 2) == sm.SM_ERR_ARG
-    assert _err(sm.sm_local_gemm, p3, _fb(128, ptr=FAKE + 8), B, Cs) == sm.SM_ERR_ALIGN
-    assert _err(sm.sm_local_gemm, p3, _fb(130), B, Cs) == sm.SM_ERR_ALIGN
-    assert _err(sm.sm_local_gemm, p3, _fb(120), B, Cs) == sm.SM_ERR_SHAPE
-    assert _err(sm.sm_local_gemm, p3, _fb(128, elems=64 * 128 - 1), B, Cs) == sm.SM_ERR_SHAPE
+    assert _err(sm.sm_local_gemm, p3, _fb(128, ptr=FAKE + 8, dt=BF), B, Cs) == sm.SM_ERR_ALIGN
+    assert _err(sm.sm_local_gemm, p3, _fb(130, dt=BF), B, Cs) == sm.SM_ERR_ALIGN
+    assert _err(sm.sm_local_gemm, p3, _fb(120, dt=BF), B, Cs) == sm.SM_ERR_SHAPE
+    assert _err(sm.sm_local_gemm, p3, _fb(128, elems=64 * 128 - 1, dt=BF), B, Cs) == sm.SM_ERR_SHAPE
     assert _err(sm.sm_local_gemm, p3, A, B, _fb(64, 64 * 64, elems=2 * 64 * 64 - 1)) == sm.SM_ERR_SHAPE
     assert _err(sm.sm_local_gemm, p3, A, B, _fb(64, 63 * 64)) == sm.SM_ERR_SHAPE
     assert _err(sm.sm_local_gemm, p1, A, B, _fb(62)) == sm.SM_ERR_ALIGN
@@ -279,16 +282,16 @@ def test_fused_reduce_validation():
     p1 = sm.sm_plan({"X": 2}, "P('X', None)", "P()", 64, 128, 64)
     p2 = sm.sm_plan({"X": 2}, "P(None, 'X')", "P()", 64, 128, 64)
     sk = sm.sm_plan({"X": 2}, "P(None, 'X')", "P('X', None)", 16, 128, 64)
-    A, B, out = _fb(128), _fb(64), _fb(64)
+    A, B, out = _fb(128, dt=BF), _fb(64, dt=BF), _fb(64)
     assert _err(sm.sm_local_gemm_reduce, p1, A, B, out) == sm.SM_ERR_CASE
     assert _err(sm.sm_local_gemm_reduce, p2, A, B, out) == sm.SM_ERR_NEEDS_GATHER
-    assert _err(sm.sm_local_gemm_reduce, p3, _fb(128, 64 * 128), B, out) == sm.SM_ERR_ARG
+    assert _err(sm.sm_local_gemm_reduce, p3, _fb(128, 64 * 128, dt=BF), B, out) == sm.SM_ERR_ARG
     assert _err(sm.sm_local_gemm_reduce, sk, A, B, out) == sm.SM_ERR_SHAPE
     assert _err(sm.sm_local_gemm_reduce, p3, A, B, out, 9) == sm.SM_ERR_ARG
     assert _err(sm.sm_local_gemm_reduce, p3, A, B, _fb(64, 16 * 64, elems=2 * 16 * 64), sm.SM_REDUCESCATTER) \
         == sm.SM_ERR_SHAPE
     q = sm.sm_plan({"X": 3}, "P(None, 'X')", "P('X', None)", 64, 96, 64)
-    assert _err(sm.sm_local_gemm_reduce, q, _fb(96), B, out, sm.SM_REDUCESCATTER) == sm.SM_ERR_INDIVISIBLE
+    assert _err(sm.sm_local_gemm_reduce, q, _fb(96, dt=BF), B, out, sm.SM_REDUCESCATTER) == sm.SM_ERR_INDIVISIBLE
 
 
 def test_reduce_and_gather_validation():
@@ -327,3 +330,31 @@ def test_sp_tail_and_reshard_validation():
         == sm.SM_ERR_INDIVISIBLE
     assert _err(rs, {"X": 2}, "A[I_X, J_X]", "P()", 8, 8, sm.SM_F32, _fb(8, 32), _fb(8)) == sm.SM_ERR_AXIS_REUSED
     assert _err(rs, {"X": 2}, "A[I, J_X]", "P()", 8, 8, 7, _fb(8, 32), _fb(8)) == sm.SM_ERR_DTYPE
+
+
+def test_buffer_element_type_is_checked():
+    """A buffer is never addressed as another element type than it holds:
+    a bfloat16 buffer given as the float32 output of a product (half the
+    bytes the call would write), or float32 data given as a bfloat16 operand,
+    is refused before anything is enqueued."""
+    p = sm.sm_plan({"T": 4}, "P(None, None)", "P(None, 'T')", 64, 64, 256)  # fp32 output
+    A, B = _fb(64, dt=BF), _fb(256, dt=BF)
+    assert _err(sm.sm_local_gemm, p, A, B, _fb(256, dt=BF)) == sm.SM_ERR_DTYPE
+    assert "bfloat16" in sm.sm_last_error() and "float32" in sm.sm_last_error()
+    assert _err(sm.sm_local_gemm, p, _fb(64, dt=F32), B, _fb(256)) == sm.SM_ERR_DTYPE
+    assert _err(sm.sm_local_gemm, p, A, B, _fb(256, dt=7)) == sm.SM_ERR_DTYPE
+    pb = sm.sm_plan({"T": 4}, "P(None, None)", "P(None, 'T')", 64, 64, 256, sm.SM_BF16, sm.SM_BF16)
+    assert _err(sm.sm_local_gemm, pb, A, B, _fb(256, dt=F32), sm.SM_EPI_GELU_TANH) == sm.SM_ERR_DTYPE
+    p3 = sm.sm_plan({"X": 2}, "P(None, 'X')", "P('X', None)", 8, 16, 8)
+    assert _err(sm.sm_reduce_partials, p3, _fb(8, 64, dt=BF), _fb(8)) == sm.SM_ERR_DTYPE
+    assert _err(sm.sm_reshard, {"X": 2}, "A[I, J_X]", "A[I_X, J]", 8, 8, sm.SM_F32, _fb(8, 32, dt=BF),
+                _fb(8, 32)) == sm.SM_ERR_DTYPE
+
+
+def test_binding_sets_buffer_element_type():
+    import torch
+
+    assert sm.buf(torch.zeros(4, 8, dtype=torch.bfloat16)).dtype == sm.SM_BF16
+    assert sm.buf(torch.zeros(2, 4, 8)).dtype == sm.SM_F32
+    with pytest.raises(ValueError):
+        sm.buf(torch.zeros(4, 8, dtype=torch.float16))

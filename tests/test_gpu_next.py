@@ -119,7 +119,7 @@ def test_fused_reduce_bitexact(case, mode):
         blocks, rows = q.n_groups * N, m // N
     stride = (rows + 3) * n
     fs = torch.full((blocks * stride + 64,), float("nan"), device=DEV)
-    s = sm.sm_buf(fs.data_ptr(), n, stride, fs.numel())
+    s = sm.sm_buf(fs.data_ptr(), n, stride, fs.numel(), sm.SM_F32, 0)
     sm.sm_local_gemm_reduce(p, sm.buf(Ad), sm.buf(Bd), s, mode)
     fsn = fs.cpu().numpy()
     if mode == sm.SM_ALLREDUCE:
