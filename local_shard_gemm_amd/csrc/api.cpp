@@ -147,8 +147,11 @@ extern "C" int32_t sm_local_gemm(const sm_plan_t* plan, const sm_buf* A, const s
   L.split_rows = L.M;  // one plain block per unit
   L.split_stride = 0;
   L.vec_ok = 1;
-  for (const Item& it : items)
+  L.vec_c = 1;
+  for (const Item& it : items) {
     if (reinterpret_cast<uintptr_t>(it.ptrs.a) % 16 || reinterpret_cast<uintptr_t>(it.ptrs.b) % 16) L.vec_ok = 0;
+    if (reinterpret_cast<uintptr_t>(it.ptrs.c) % 8) L.vec_c = 0;
+  }
   const bool skinny = m <= kSkinnyMaxM;
   hipStream_t s = static_cast<hipStream_t>(stream);
   for (size_t first = 0; first < items.size(); first += kMaxUnitsPerLaunch) {
@@ -410,6 +413,7 @@ extern "C" int32_t sm_local_gemm_reduce(const sm_plan_t* plan, const sm_buf* A, 
   L.split_rows = split ? static_cast<int32_t>(orows) : L.M;
   L.split_stride = split ? out->block_stride : 0;
   L.vec_ok = 1;
+  L.vec_c = 1;
 
   struct Item {
     int32_t b_id, a_row;
@@ -445,6 +449,7 @@ extern "C" int32_t sm_local_gemm_reduce(const sm_plan_t* plan, const sm_buf* A, 
     it.ptrs.b = static_cast<const uint16_t*>(B->ptr) + rb.offset;
     it.ptrs.c = static_cast<float*>(out->ptr) + coff;
     if (reinterpret_cast<uintptr_t>(it.ptrs.a) % 16 || reinterpret_cast<uintptr_t>(it.ptrs.b) % 16) L.vec_ok = 0;
+    if (reinterpret_cast<uintptr_t>(it.ptrs.c) % 8) L.vec_c = 0;
     items.push_back(it);
   }
   std::stable_sort(items.begin(), items.end(), [](const Item& x, const Item& y) {

@@ -86,12 +86,15 @@ __device__ __forceinline__ void transpose8(const uint4 (&in)[8], uint4 (&out)[8]
 // GeLU, tanh form: 0.5 x (1 + tanh(z)), z = sqrt(2/pi) (x + 0.044715 x^3),
 // evaluated as x / (1 + exp(-2 z)) -- the same function (1 + tanh(z) =
 // 2 / (1 + exp(-2z))) without the float32 cancellation of 1 + tanh(z) for
-// negative z.
+// negative z. exp(-2z) = 2^(-2z log2(e)) on the hardware exp2, and the
+// division as a hardware reciprocal: each adds about one float32 ulp, far
+// below the bfloat16 rounding of the stored H.
 __device__ __forceinline__ float gelu_tanh_f32(float x) {
   const float k0 = 0.7978845608028654f;  // sqrt(2/pi)
   const float k1 = 0.044715f;
+  const float m2log2e = -2.0f * 1.4426950408889634f;
   const float z = k0 * (x + k1 * x * x * x);
-  return x / (1.0f + expf(-2.0f * z));
+  return x * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(m2log2e * z));
 }
 
 // float -> bfloat16, round to nearest even (NaN stays NaN).
@@ -121,33 +124,82 @@ __device__ __forceinline__ void tile_of(int w, int T, int VR, int VC, int* vr, i
   *vc = idx / rows;
 }
 
+// One 32x32 block of v_mfma_f32_32x32x16_bf16. TRANS puts the B fragment
+// first, so the block accumulates C^T (see store_tile).
+template <bool TRANS>
+__device__ __forceinline__ f32x16 mfma_block(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+  return TRANS ? __builtin_amdgcn_mfma_f32_32x32x16_bf16(b, a, c, 0, 0, 0)
+               : __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// Epilogue of a 256x256 tile (wave (wm, wn) owns a 128x128 sub-tile of
+// 4x4 blocks of 32x32).
+//  * float32 output: blocks accumulate C, register v of lane l holding
+//    C[.. + 8(v/4) + 4(l/32) + v%4][.. + l%32]; each store instruction
+//    writes two full 128-byte row segments (32 lanes x 4 bytes per row).
+//  * bfloat16 output: blocks accumulate C^T (mfma_block<true>), register
+//    4g + e of lane l holding C[.. + l%32][.. + 8g + 4(l/32) + e]: four
+//    consecutive columns of one row, one 8-byte store when every C view is
+//    8-byte aligned (L.vec_c) -- a quarter of the store instructions of
+//    element-wise 2-byte stores.
 template <bool OUT_BF16, bool GELU, bool EDGE>
 __device__ __forceinline__ void store_tile(const f32x16 (&acc)[4][4], void* C, const GemmLaunch& L, int row0,
                                            int col0) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
-  const int rsub = 4 * (lane >> 5), csub = lane & 31;
   const int M = L.M, N = L.N;
   const int64_t ldc = L.ldc;
   const bool split = L.split_rows < M;
+  auto row_off = [&](int r) -> int64_t {
+    return split ? (r / L.split_rows) * L.split_stride + static_cast<int64_t>(r % L.split_rows) * ldc
+                 : static_cast<int64_t>(r) * ldc;
+  };
+  if constexpr (!OUT_BF16) {
+    const int rsub = 4 * (lane >> 5), csub = lane & 31;
 #pragma unroll
-  for (int mi = 0; mi < 4; ++mi)
+    for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
-    for (int ni = 0; ni < 4; ++ni)
+      for (int ni = 0; ni < 4; ++ni)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int r = row0 + wm * 128 + mi * 32 + 8 * (v >> 2) + rsub + (v & 3);
-        const int c = col0 + wn * 128 + ni * 32 + csub;
-        if (EDGE && (r >= M || c >= N)) continue;
-        float x = acc[mi][ni][v];
-        if (GELU) x = gelu_tanh_f32(x);
-        const int64_t off = split ? (r / L.split_rows) * L.split_stride + static_cast<int64_t>(r % L.split_rows) * ldc + c
-                                  : static_cast<int64_t>(r) * ldc + c;
-        if (OUT_BF16)
-          static_cast<uint16_t*>(C)[off] = bf16_rne(x);
-        else
-          static_cast<float*>(C)[off] = x;
-      }
+        for (int v = 0; v < 16; ++v) {
+          const int r = row0 + wm * 128 + mi * 32 + 8 * (v >> 2) + rsub + (v & 3);
+          const int c = col0 + wn * 128 + ni * 32 + csub;
+          if (EDGE && (r >= M || c >= N)) continue;
+          float x = acc[mi][ni][v];
+          if (GELU) x = gelu_tanh_f32(x);
+          static_cast<float*>(C)[row_off(r) + c] = x;
+        }
+  } else {
+    const int rl = lane & 31, cq = 4 * (lane >> 5);
+    const bool vec = L.vec_c != 0;
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi) {
+      const int r = row0 + wm * 128 + mi * 32 + rl;
+      if (EDGE && r >= M) continue;
+      const int64_t roff = row_off(r);
+#pragma unroll
+      for (int ni = 0; ni < 4; ++ni)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int c = col0 + wn * 128 + ni * 32 + 8 * g + cq;
+          uint32_t h[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            float x = acc[mi][ni][4 * g + e];
+            if (GELU) x = gelu_tanh_f32(x);
+            h[e] = bf16_rne(x);
+          }
+          uint16_t* dst = static_cast<uint16_t*>(C) + roff + c;
+          if (vec && (!EDGE || c + 3 < N)) {
+            *reinterpret_cast<uint2*>(dst) = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (!EDGE || c + e < N) dst[e] = static_cast<uint16_t>(h[e]);
+          }
+        }
+    }
+  }
 }
 
 template <bool EDGE, bool OUT_BF16, bool GELU>
@@ -228,7 +280,7 @@ __device__ __forceinline__ void run_tile(const GemmLaunch& L, const uint16_t* __
       for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
         for (int ni = 0; ni < 4; ++ni)
-          acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mi], bfv[ni], acc[mi][ni], 0, 0, 0);
+          acc[mi][ni] = mfma_block<OUT_BF16>(af[mi], bfv[ni], acc[mi][ni]);
     }
   };
 
@@ -378,7 +430,7 @@ __device__ __forceinline__ void run_tile_lds(const GemmLaunch& L, const uint16_t
     for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
       for (int ni = 0; ni < 4; ++ni)
-        acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(F.a[mi], F.b[ni], acc[mi][ni], 0, 0, 0);
+        acc[mi][ni] = mfma_block<OUT_BF16>(F.a[mi], F.b[ni], acc[mi][ni]);
   };
 
   const int nk = L.K / BK2;
@@ -444,7 +496,7 @@ __device__ __forceinline__ void run_tile_lds(const GemmLaunch& L, const uint16_t
 #pragma unroll
     for (int idx = 0; idx < 16; ++idx) {
       const int mi = idx >> 2, ni = idx & 3;
-      acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur.a[mi], cur.b[ni], acc[mi][ni], 0, 0, 0);
+      acc[mi][ni] = mfma_block<OUT_BF16>(cur.a[mi], cur.b[ni], acc[mi][ni]);
       if (idx < 6) {
         read_item(nxt, st_next, s_next, 2 * idx);
         read_item(nxt, st_next, s_next, 2 * idx + 1);

@@ -76,15 +76,15 @@ __device__ __forceinline__ void transpose8(const uint4 (&in)[8], uint4 (&out)[8]
   }
 }
 
-// GeLU, tanh form: 0.5 x (1 + tanh(z)), z = sqrt(2/pi) (x + 0.044715 x^3),
-// evaluated as x / (1 + exp(-2 z)) -- the same function (1 + tanh(z) =
-// 2 / (1 + exp(-2z))) without the float32 cancellation of 1 + tanh(z) for
-// negative z.
+// GeLU, tanh form, evaluated exactly as in the MFMA GEMM's epilogue:
+// x / (1 + exp(-2z)) with z = sqrt(2/pi) (x + 0.044715 x^3), the exponential
+// on the hardware exp2 and the division as a hardware reciprocal.
 __device__ __forceinline__ float gelu_tanh_f32(float x) {
   const float k0 = 0.7978845608028654f;  // sqrt(2/pi)
   const float k1 = 0.044715f;
+  const float m2log2e = -2.0f * 1.4426950408889634f;
   const float z = k0 * (x + k1 * x * x * x);
-  return x / (1.0f + expf(-2.0f * z));
+  return x * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(m2log2e * z));
 }
 
 __device__ __forceinline__ uint16_t bf16_rne(float x) {

@@ -136,6 +136,62 @@ def test_ragged_shapes_bitexact(case):
         assert torch.equal(g, g2)
 
 
+def test_store_paths_bitexact():
+    """The MFMA kernels' epilogue stores 4 consecutive columns per lane as
+    one vector when the output views allow it. Covered here: (a) a logical
+    width that is not a multiple of 4 inside padded stacked blocks (the last
+    run of a row falls back to single elements, and the padding columns stay
+    untouched); (b) column-block views that start off the 16-byte grid (every
+    store falls back to single elements)."""
+    say("case: store paths")
+    # (a) case 3, n = 70 inside blocks of ld 72
+    I, J, K = 300, 2 * 96, 70
+    A, B = _int((I, J), 41), _int((J, K), 42)
+    p, q = _plans({"Y": 2}, "P(None, 'Y')", "P('Y', None)", I, J, K)
+    ld = 72
+    Bp = torch.zeros(J, ld, dtype=torch.bfloat16)
+    Bp[:, :K] = B
+    full = torch.full((2 * I * ld + 256,), float("nan"), device=DEV)
+    C = full[:2 * I * ld].view(2, I, ld)
+    sm.sm_local_gemm(p, sm.buf(to_dev(A)), sm.buf(to_dev(Bp)), sm.buf(C, ld=ld))
+    Cn = C.cpu().numpy()
+    for u in range(2):
+        assert f32_bits_equal(Cn[u, :, :K], ref.unit_partial(q, A, B, u)), u
+    assert np.isnan(Cn[:, :, K:]).all()
+    assert bool(torch.isnan(full[2 * I * ld:]).all())
+    # (b) case 1, global layout, column blocks of width 6 (views at 24-byte steps)
+    I, J, K = 260, 64, 2 * 6
+    A, B = _int((I, J), 43), _int((J, K), 44)
+    p, q = _plans({"Y": 2}, "P()", "P(None, 'Y')", I, J, K)
+    Bp = torch.zeros(J, 16, dtype=torch.bfloat16)
+    Bp[:, :K] = B
+    fg, g = guarded((I, K), torch.float32)
+    sm.sm_local_gemm(p, sm.buf(to_dev(A)), sm.buf(to_dev(Bp)), sm.buf(g))
+    assert f32_bits_equal(g.cpu().numpy(), ref.dense(A, B))
+    assert guard_intact(fg, g.numel())
+
+
+def test_gelu_epilogue_unaligned_views():
+    """GeLU -> bfloat16 into the global H layout with column blocks of width 6:
+    half of the views start off the 8-byte grid, so the bfloat16 stores go
+    element by element; H is within the derived bound of the oracle."""
+    say("case: gelu epilogue unaligned views")
+    X = wl.random_normal((96, 64), 45)
+    W1 = wl.random_normal((64, 24), 46, 0.1)
+    W2 = wl.random_normal((24, 64), 47, 0.1)
+    p1, q1 = _plans({"T": 4}, "P(None, None)", "P(None, 'T')", 96, 64, 24, sm.SM_BF16)
+    _, q2 = _plans({"T": 4}, "P(None, 'T')", "P('T', None)", 96, 24, 64)
+    fh = torch.zeros(96 * 24 + 64, dtype=torch.bfloat16, device=DEV)
+    H = fh[:96 * 24].view(96, 24)
+    sm.sm_local_gemm(p1, sm.buf(to_dev(X)), sm.buf(to_dev(W1)), sm.buf(H), sm.SM_EPI_GELU_TANH)
+    Hw, _ = ref.mlp_chain(q1, q2, X, W1, W2)
+    Hg = H.cpu().view(torch.int16).numpy().view(np.uint16)
+    absdot = ref.matmul(np.abs(ref.widen(X)), np.abs(ref.widen(W1)))
+    assert gelu_h_within_bound(Hg, Hw, absdot, 64).all()
+    assert (Hg != Hw).mean() < 0.01
+    assert bool((fh[96 * 24:] == 0).all())
+
+
 SKINNY = [
     ({"T": 4}, "P(None, 'T')", "P('T', None)", 5, 4 * 100, 296),    # ragged K and N
     ({"T": 8}, "P(None, 'T')", "P('T', None)", 16, 8 * 256, 1024),  # full tiles
