@@ -232,6 +232,7 @@ def test_sp_tail_full_downproj():
 
 RESHARD = [
     ({"X": 4}, "A[I, J_X]", "A[I_X, J]", 512, 768),       # all-to-all
+    ({"X": 4}, "A[I, J_X]", "A[I_X, J]", 4104, 96),       # 16 jobs of 1026 short rows, copied in source order
     ({"X": 2, "Y": 2}, "A[I_XY, J]", "A[I_X, J_Y]", 256, 512),
     ({"X": 4}, "A[I_X, J]", "P()", 256, 264),             # all-gather to replicated
     ({"X": 2, "Y": 3}, "A[I, J_X]", "A[I, J_Y]", 64, 48),  # blocks straddle blocks

@@ -192,6 +192,23 @@ def test_gelu_epilogue_unaligned_views():
     assert bool((fh[96 * 24:] == 0).all())
 
 
+def test_gather_many_short_rows_bitexact():
+    """Case-1 blocks of 1030 x 40 fp32 gathered into C[4120, 80]: 8240 short
+    rows in 8 jobs, most lanes of each row's workgroup idle; the gathered C
+    equals the dense product bit for bit and nothing outside C is written."""
+    I, J, K = 4 * 1030, 64, 2 * 40
+    say("case: gather many short rows")
+    A, B = _int((I, J), 51), _int((J, K), 52)
+    p, q = _plans({"X": 4, "Y": 2}, "P('X', None)", "P(None, 'Y')", I, J, K)
+    Bp = torch.zeros(J, 88, dtype=torch.bfloat16)
+    Bp[:, :K] = B
+    _, P = run_partials(p, to_dev(A), to_dev(Bp))
+    fg, g = guarded((I, K), torch.float32)
+    sm.sm_gather_shards(p, sm.SM_WHAT_C_BLOCKS, sm.buf(P), sm.buf(g))
+    assert f32_bits_equal(g.cpu().numpy(), ref.dense(A, B))
+    assert guard_intact(fg, g.numel())
+
+
 SKINNY = [
     ({"T": 4}, "P(None, 'T')", "P('T', None)", 5, 4 * 100, 296),    # ragged K and N
     ({"T": 8}, "P(None, 'T')", "P('T', None)", 16, 8 * 256, 1024),  # full tiles
