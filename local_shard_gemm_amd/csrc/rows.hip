@@ -183,14 +183,37 @@ __global__ __launch_bounds__(NT) void rows_layernorm_kernel(const RowLaunch L, c
   const int n4 = J.cols >> 2;
   float4 v[V];
   float s = 0.f;
+  // Few partials and short rows (NS * V <= 16 vectors per thread): every
+  // load of the row is issued before the rank-ordered adds, so they are all
+  // in flight together. Otherwise partials are added as they arrive.
+  constexpr bool kAllFirst = NS > 0 && NS * V <= 16;
+  if constexpr (kAllFirst) {
+    float4 t[kAllFirst ? NS : 1][V];
 #pragma unroll
-  for (int i = 0; i < V; ++i) {
-    const int c4 = threadIdx.x + i * NT;
-    v[i] = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (c4 < n4) {
-      v[i] = ldnt(reinterpret_cast<const float4*>(src) + c4);
-      for (int y = 1; y < nsum; ++y) add4(v[i], ldnt(reinterpret_cast<const float4*>(src + y * J.src_stride) + c4));
+    for (int y = 0; y < NS; ++y)
+#pragma unroll
+      for (int i = 0; i < V; ++i) {
+        const int c4 = threadIdx.x + i * NT;
+        t[y][i] = c4 < n4 ? ldnt(reinterpret_cast<const float4*>(src + y * J.src_stride) + c4)
+                          : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+#pragma unroll
+    for (int i = 0; i < V; ++i) {
+      v[i] = t[0][i];
+#pragma unroll
+      for (int y = 1; y < NS; ++y) add4(v[i], t[y][i]);
       s += (v[i].x + v[i].y) + (v[i].z + v[i].w);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < V; ++i) {
+      const int c4 = threadIdx.x + i * NT;
+      v[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (c4 < n4) {
+        v[i] = ldnt(reinterpret_cast<const float4*>(src) + c4);
+        for (int y = 1; y < nsum; ++y) add4(v[i], ldnt(reinterpret_cast<const float4*>(src + y * J.src_stride) + c4));
+        s += (v[i].x + v[i].y) + (v[i].z + v[i].w);
+      }
     }
   }
   const float inv_n = 1.0f / static_cast<float>(J.cols);
