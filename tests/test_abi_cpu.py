@@ -358,3 +358,24 @@ def test_binding_sets_buffer_element_type():
     assert sm.buf(torch.zeros(2, 4, 8)).dtype == sm.SM_F32
     with pytest.raises(ValueError):
         sm.buf(torch.zeros(4, 8, dtype=torch.float16))
+
+
+def test_empty_inputs_refused():
+    """Zero-sized dimensions and empty unit / group ranges are refused on the
+    host (the ABI computes on M, N, K >= 1), by the library and the oracle's
+    planner alike."""
+    for I, J, K in ((0, 8, 8), (8, 0, 8), (8, 8, 0)):
+        with pytest.raises(sm.ShardmmError) as ei:
+            sm.sm_plan({"X": 2}, "P()", "P()", I, J, K)
+        assert ei.value.status == sm.SM_ERR_SHAPE
+        with pytest.raises(ref_planner.PlanError) as pe:
+            ref_planner.plan({"X": 2}, "P()", "P()", I, J, K)
+        assert pe.value.code == "SHAPE"
+    p1 = sm.sm_plan({"X": 2}, "P('X', None)", "P()", 64, 128, 64)
+    p3 = sm.sm_plan({"X": 2}, "P(None, 'X')", "P('X', None)", 64, 128, 64)
+    A, B = _fb(128, dt=BF), _fb(64, dt=BF)
+    assert _err(sm.sm_local_gemm, p1, A, B, _fb(64, 32 * 64), 0, 0, 0) == sm.SM_ERR_ARG
+    assert _err(sm.sm_reduce_partials, p3, _fb(64, 64 * 64), _fb(64), 0, 0, 0) == sm.SM_ERR_ARG
+    assert _err(sm.sm_local_gemm_reduce, p3, A, B, _fb(64), 0, 0, 0) == sm.SM_ERR_ARG
+    assert _err(sm.sm_reshard, {"X": 2}, "A[I, J_X]", "A[I_X, J]", 0, 8, sm.SM_F32, _fb(8, 32), _fb(8, 32)) \
+        == sm.SM_ERR_SHAPE

@@ -209,6 +209,50 @@ def test_gather_many_short_rows_bitexact():
     assert guard_intact(fg, g.numel())
 
 
+def test_many_units_and_jobs_bitexact():
+    """Maximum batch sizes: 128 units in one sm_local_gemm call (two launches
+    of at most 64 units), gathered through 128 row jobs (four launches of at
+    most 32); and an 80-unit case 3 reduced through 80 row jobs, both modes."""
+    say("case: many units and jobs")
+    # case 1 on {X:16, Y:8}: 128 blocks of [24, 16]
+    I, J, K = 16 * 24, 64, 8 * 16
+    A, B = _int((I, J), 61), _int((J, K), 62)
+    p, q = _plans({"X": 16, "Y": 8}, "P('X', None)", "P(None, 'Y')", I, J, K)
+    assert p.n_units == 128
+    full, P = run_partials(p, to_dev(A), to_dev(B))
+    fg, g = guarded((I, K), torch.float32)
+    sm.sm_gather_shards(p, sm.SM_WHAT_C_BLOCKS, sm.buf(P), sm.buf(g))
+    assert f32_bits_equal(g.cpu().numpy(), ref.dense(A, B))
+    assert guard_intact(full, P.numel()) and guard_intact(fg, g.numel())
+    # case 3 on {X:40, Y:2}: 40 groups x 2 partials of [32, 48]
+    I, J, K = 40 * 32, 2 * 64, 48
+    A, B = _int((I, J), 63), _int((J, K), 64)
+    p, q = _plans({"X": 40, "Y": 2}, "P('X', 'Y')", "P('Y', None)", I, J, K)
+    assert p.n_units == 80
+    _, P = run_partials(p, to_dev(A), to_dev(B))
+    want = ref.dense(A, B)
+    for mode in (sm.SM_ALLREDUCE, sm.SM_REDUCESCATTER):
+        fo, out = guarded((I, K), torch.float32)
+        sm.sm_reduce_partials(p, sm.buf(P), sm.buf(out), mode)
+        assert f32_bits_equal(out.cpu().numpy(), want), mode
+        assert guard_intact(fo, out.numel())
+
+
+def test_single_partial_reduce_bitexact():
+    """Degenerate case 3: J split over an axis of size 1 (N = 1). The reduce
+    is a copy of the one partial, in both modes."""
+    say("case: N = 1 reduce")
+    I, J, K = 96, 64, 40
+    A, B = _int((I, J), 65), _int((J, K), 66)
+    p, q = _plans({"X": 1}, "P(None, 'X')", "P('X', None)", I, J, K)
+    assert p.kase == sm.SM_CASE3 and p.n_partials == 1
+    _, P = run_partials(p, to_dev(A), to_dev(B))
+    for mode in (sm.SM_ALLREDUCE, sm.SM_REDUCESCATTER):
+        out = torch.full((I, K), float("nan"), device=DEV)
+        sm.sm_reduce_partials(p, sm.buf(P), sm.buf(out), mode)
+        assert f32_bits_equal(out.cpu().numpy(), ref.dense(A, B)), mode
+
+
 SKINNY = [
     ({"T": 4}, "P(None, 'T')", "P('T', None)", 5, 4 * 100, 296),    # ragged K and N
     ({"T": 8}, "P(None, 'T')", "P('T', None)", 16, 8 * 256, 1024),  # full tiles
