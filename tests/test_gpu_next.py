@@ -228,6 +228,42 @@ def test_sp_tail_full_downproj():
         assert ref.rel_frobenius(got, want) <= LN_TOL
 
 
+def test_sp_tail_full_mlp_with_affine():
+    """The tail as the benchmark runs it: the MLP's 4 partials [4096, 4096]
+    (from the two-layer chain on the full workload), reduce-scattered, layer
+    normed with gamma and beta, all-gathered; sampled rows of every owner
+    within the float tolerance of the oracle."""
+    w = wl.get("mlp")
+    say("case: sp tail full mlp")
+    X = wl.make_operand(w.operand("X"))
+    W1 = wl.make_operand(w.operand("W1"))
+    W2 = wl.make_operand(w.operand("W2"))
+    B_, D = X.shape
+    F = W1.shape[1]
+    p1 = sm.sm_plan(dict(w.mesh), w.operand("X").spec, w.operand("W1").spec, B_, D, F, out_dtype=sm.SM_BF16)
+    p2 = sm.sm_plan(dict(w.mesh), "P(None, 'T')", w.operand("W2").spec, B_, F, D)
+    q2 = planner.plan(dict(w.mesh), "P(None, 'T')", w.operand("W2").spec, B_, F, D)
+    H = torch.empty(B_, F, dtype=torch.bfloat16, device=DEV)
+    sm.sm_local_gemm(p1, sm.buf(to_dev(X)), sm.buf(to_dev(W1)), sm.buf(H), sm.SM_EPI_GELU_TANH)
+    _, P = run_partials(p2, H, to_dev(W2))
+    rng = np.random.default_rng(811)
+    gamma = rng.standard_normal(D).astype(np.float32)
+    beta = rng.standard_normal(D).astype(np.float32)
+    out = torch.empty(B_, D, device=DEV)
+    sm.sm_reduce_scatter_layernorm(p2, sm.buf(P), sm.buf(out), torch.from_numpy(gamma).to(DEV),
+                                   torch.from_numpy(beta).to(DEV), 1e-5)
+    # oracle: the partials from the GPU's own H (H itself is checked against
+    # the oracle in the MLP tests), summed in rank order, then layer norm
+    Hn = H.cpu()
+    m = q2.c_local[0] // q2.n_partials
+    for y in range(q2.n_partials):
+        rows = [y * m + r for r in sample_rows(m, 3, 820 + y)]
+        parts = [ref.unit_partial(q2, Hn, W2, u, rows=rows) for u in range(q2.n_units)]
+        want = ref.layer_norm(ref.sum_ranked(parts), gamma, beta, 1e-5)
+        got = out[rows].cpu().numpy()
+        assert ref.rel_frobenius(got, want) <= LN_TOL, y
+
+
 # ------------------------------------------------------------------ f4
 
 RESHARD = [
@@ -237,6 +273,22 @@ RESHARD = [
     ({"X": 4}, "A[I_X, J]", "P()", 256, 264),             # all-gather to replicated
     ({"X": 2, "Y": 3}, "A[I, J_X]", "A[I, J_Y]", 64, 48),  # blocks straddle blocks
 ]
+
+
+def test_reshard_full_size_bitexact():
+    """The all-to-all as the benchmark runs it: bf16 [4096, 4096] A[I,J_X] ->
+    A[I_X,J] on {X:4}, stacked blocks in and out, bit for bit."""
+    say("case: reshard full size")
+    X = wl.random_normal((4096, 4096), 961)
+    mesh = {"X": 4}
+    src_blocks = ref.shard(ref.stored(X)[0], mesh, "A[I, J_X]")
+    src = to_dev(torch.from_numpy(np.stack([src_blocks[b] for b in sorted(src_blocks)])).view(torch.bfloat16))
+    dst = torch.empty(4, 1024, 4096, dtype=torch.bfloat16, device=DEV)
+    sm.sm_reshard(mesh, "A[I, J_X]", "A[I_X, J]", 4096, 4096, sm.SM_BF16, sm.buf(src), sm.buf(dst))
+    want = ref.reshard(src_blocks, mesh, "A[I, J_X]", "A[I_X, J]", 4096, 4096)
+    got = ref.stored(dst.cpu())[0]
+    for b in range(4):
+        np.testing.assert_array_equal(got[b], want[b])
 
 
 @pytest.mark.parametrize("case", RESHARD, ids=lambda c: f"{c[1]}->{c[2]}")
