@@ -34,13 +34,14 @@ int32_t check_buf_basic(const sm_buf* b, const char* what, int32_t dtype) {
   return SM_OK;
 }
 
-// A block at `offset` spanning rows x cols must lie inside the buffer.
+// A block at `offset` spanning rows x cols must lie inside the buffer. The
+// end is computed in 128 bits, so no caller-supplied size can wrap it.
 int32_t check_extent(const sm_buf* b, const BlockRef& r, const char* what) {
   if (r.cols > b->ld) return fail(SM_ERR_SHAPE, std::string(what) + ": ld smaller than the block width");
-  const int64_t last = r.offset + (r.rows - 1) * b->ld + r.cols;
-  if (r.offset < 0 || last > b->elems)
-    return fail(SM_ERR_SHAPE, std::string(what) + ": block extends past the buffer (" + std::to_string(last) +
-                                  " > " + std::to_string(b->elems) + " elements)");
+  const __int128 last = static_cast<__int128>(r.offset) + static_cast<__int128>(r.rows - 1) * b->ld + r.cols;
+  if (r.offset < 0 || r.rows < 1 || last > b->elems)
+    return fail(SM_ERR_SHAPE, std::string(what) + ": block extends past the buffer (" + std::to_string(b->elems) +
+                                  " elements)");
   return SM_OK;
 }
 
@@ -48,7 +49,7 @@ int32_t check_extent(const sm_buf* b, const BlockRef& r, const char* what) {
 // for inputs but kept uniform).
 int32_t check_stacked(const sm_buf* b, int64_t rows, int64_t cols, const char* what) {
   if (cols > b->ld) return fail(SM_ERR_SHAPE, std::string(what) + ": ld smaller than the block width");
-  if (b->block_stride < rows * b->ld)
+  if (static_cast<__int128>(b->block_stride) < static_cast<__int128>(rows) * b->ld)
     return fail(SM_ERR_SHAPE, std::string(what) + ": block_stride smaller than rows * ld");
   return SM_OK;
 }
@@ -111,9 +112,10 @@ extern "C" int32_t sm_local_gemm(const sm_plan_t* plan, const sm_buf* A, const s
     rc.cols = n;
     const int32_t a_id = v.a_block[0] * p.a_grid[1] + v.a_block[1];
     const int32_t b_id = v.b_block[0] * p.b_grid[1] + v.b_block[1];
-    ra.offset = A->block_stride ? a_id * A->block_stride : v.a_row0 * A->ld + v.a_col0;
-    rb.offset = B->block_stride ? b_id * B->block_stride : v.b_row0 * B->ld + v.b_col0;
-    rc.offset = C->block_stride ? static_cast<int64_t>(u - unit_begin) * C->block_stride : v.c_row0 * C->ld + v.c_col0;
+    ra.offset = A->block_stride ? static_cast<i128>(a_id) * A->block_stride : static_cast<i128>(v.a_row0) * A->ld + v.a_col0;
+    rb.offset = B->block_stride ? static_cast<i128>(b_id) * B->block_stride : static_cast<i128>(v.b_row0) * B->ld + v.b_col0;
+    rc.offset = C->block_stride ? static_cast<i128>(u - unit_begin) * C->block_stride
+                                : static_cast<i128>(v.c_row0) * C->ld + v.c_col0;
     if ((st = check_extent(A, ra, "A"))) return st;
     if ((st = check_extent(B, rb, "B"))) return st;
     if ((st = check_extent(C, rc, "C"))) return st;
@@ -121,9 +123,9 @@ extern "C" int32_t sm_local_gemm(const sm_plan_t* plan, const sm_buf* A, const s
     it.unit = u;
     it.b_id = b_id;
     it.a_row = v.a_block[0];
-    it.ptrs.a = static_cast<const uint16_t*>(A->ptr) + ra.offset;
-    it.ptrs.b = static_cast<const uint16_t*>(B->ptr) + rb.offset;
-    it.ptrs.c = static_cast<char*>(C->ptr) + rc.offset * static_cast<int64_t>(csz);
+    it.ptrs.a = static_cast<const uint16_t*>(A->ptr) + ra.off();
+    it.ptrs.b = static_cast<const uint16_t*>(B->ptr) + rb.off();
+    it.ptrs.c = static_cast<char*>(C->ptr) + rc.off() * static_cast<int64_t>(csz);
     items.push_back(it);
   }
   // Units sharing a B block go next to each other (their tiles stack into
@@ -231,7 +233,7 @@ extern "C" int32_t sm_reduce_partials(const sm_plan_t* plan, const sm_buf* parti
   if (m > INT32_MAX || n > INT32_MAX) return fail(SM_ERR_SHAPE, "block too large");
   if ((st = check_stacked(partials, m, n, "partials"))) return st;
   {
-    BlockRef last{static_cast<int64_t>(group_count) * N * partials->block_stride - partials->block_stride, m, n};
+    BlockRef last{static_cast<i128>(group_count) * N * partials->block_stride - partials->block_stride, m, n};
     if ((st = check_extent(partials, last, "partials"))) return st;
   }
   const bool rs = mode == SM_REDUCESCATTER;
@@ -255,13 +257,13 @@ extern "C" int32_t sm_reduce_partials(const sm_plan_t* plan, const sm_buf* parti
       d.rows = orows;
       d.cols = n;
       if (out->block_stride == 0)
-        d.offset = (bi * m + y * orows) * out->ld + bk * n;
+        d.offset = (static_cast<i128>(bi) * m + y * orows) * out->ld + bk * n;
       else
-        d.offset = (static_cast<int64_t>(g - group_begin) * nblk + y) * out->block_stride;
+        d.offset = (static_cast<i128>(g - group_begin) * nblk + y) * out->block_stride;
       if ((st = check_extent(out, d, "out"))) return st;
       RowJob J;
       J.src = P + src0 + y * orows * partials->ld;
-      J.dst = O + d.offset;
+      J.dst = O + d.off();
       J.src_stride = partials->block_stride;
       J.lds = partials->ld;
       J.ldd = out->ld;
@@ -347,13 +349,13 @@ extern "C" int32_t sm_gather_shards(const sm_plan_t* plan, int32_t what, const s
       r0 = (id / grid_c) * rows;
       c0 = (id % grid_c) * cols;
     }
-    BlockRef s{id * shards->block_stride, rows, cols};
-    BlockRef d{r0 * out->ld + c0, rows, cols};
+    BlockRef s{static_cast<i128>(id) * shards->block_stride, rows, cols};
+    BlockRef d{static_cast<i128>(r0) * out->ld + c0, rows, cols};
     if ((st = check_extent(shards, s, "shards"))) return st;
     if ((st = check_extent(out, d, "out"))) return st;
     RowJob J;
-    J.src = static_cast<const char*>(shards->ptr) + s.offset * static_cast<int64_t>(esz);
-    J.dst = static_cast<char*>(out->ptr) + d.offset * static_cast<int64_t>(esz);
+    J.src = static_cast<const char*>(shards->ptr) + s.off() * static_cast<int64_t>(esz);
+    J.dst = static_cast<char*>(out->ptr) + d.off() * static_cast<int64_t>(esz);
     J.src_stride = 0;
     J.lds = shards->ld;
     J.ldd = out->ld;
@@ -425,28 +427,29 @@ extern "C" int32_t sm_local_gemm_reduce(const sm_plan_t* plan, const sm_buf* A, 
     UnitView v;
     if ((st = unit_view(p, g * N, &v))) return st;
     if (v.a_col0 != 0 || v.b_row0 != 0) return fail(SM_ERR_ARG, "J slices are not contiguous from 0");
-    BlockRef ra{v.a_row0 * A->ld, m, kfull};
+    BlockRef ra{static_cast<i128>(v.a_row0) * A->ld, m, kfull};
     BlockRef rb{v.b_col0, kfull, n};
     if ((st = check_extent(A, ra, "A"))) return st;
     if ((st = check_extent(B, rb, "B"))) return st;
     int64_t coff;
     if (out->block_stride == 0) {
-      coff = v.c_row0 * out->ld + v.c_col0;
-      BlockRef rc{coff, m, n};
+      BlockRef rc{static_cast<i128>(v.c_row0) * out->ld + v.c_col0, m, n};
       if ((st = check_extent(out, rc, "out"))) return st;
+      coff = rc.off();
     } else {
       const int32_t nblk = rs ? N : 1;
-      coff = static_cast<int64_t>(g - group_begin) * nblk * out->block_stride;
+      const i128 c0 = static_cast<i128>(g - group_begin) * nblk * out->block_stride;
       for (int32_t y = 0; y < nblk; ++y) {
-        BlockRef rc{coff + y * out->block_stride, orows, n};
+        BlockRef rc{c0 + static_cast<i128>(y) * out->block_stride, orows, n};
         if ((st = check_extent(out, rc, "out"))) return st;
       }
+      coff = static_cast<int64_t>(c0);  // bounded by the checks above
     }
     Item it;
     it.b_id = v.b_block[1];
     it.a_row = v.a_block[0];
-    it.ptrs.a = static_cast<const uint16_t*>(A->ptr) + ra.offset;
-    it.ptrs.b = static_cast<const uint16_t*>(B->ptr) + rb.offset;
+    it.ptrs.a = static_cast<const uint16_t*>(A->ptr) + ra.off();
+    it.ptrs.b = static_cast<const uint16_t*>(B->ptr) + rb.off();
     it.ptrs.c = static_cast<float*>(out->ptr) + coff;
     if (reinterpret_cast<uintptr_t>(it.ptrs.a) % 16 || reinterpret_cast<uintptr_t>(it.ptrs.b) % 16) L.vec_ok = 0;
     if (reinterpret_cast<uintptr_t>(it.ptrs.c) % 8) L.vec_c = 0;

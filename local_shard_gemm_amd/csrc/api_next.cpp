@@ -40,7 +40,7 @@ extern "C" int32_t sm_reduce_scatter_layernorm(const sm_plan_t* plan, const sm_b
     return fail(SM_ERR_ALIGN, "gamma / beta not 16-byte aligned");
   if ((st = check_stacked(partials, m, n, "partials"))) return st;
   {
-    BlockRef last{static_cast<int64_t>(group_count) * N * partials->block_stride - partials->block_stride, m, n};
+    BlockRef last{static_cast<i128>(group_count) * N * partials->block_stride - partials->block_stride, m, n};
     if ((st = check_extent(partials, last, "partials"))) return st;
   }
   const int64_t orows = m / N;
@@ -56,14 +56,14 @@ extern "C" int32_t sm_reduce_scatter_layernorm(const sm_plan_t* plan, const sm_b
     const int64_t bi = g / p.c_grid[1];
     const int64_t src0 = static_cast<int64_t>(g - group_begin) * N * partials->block_stride;
     for (int32_t y = 0; y < N; ++y) {
-      BlockRef d{out->block_stride == 0 ? (bi * m + y * orows) * out->ld
-                                        : (static_cast<int64_t>(g - group_begin) * N + y) * out->block_stride,
+      BlockRef d{out->block_stride == 0 ? (static_cast<i128>(bi) * m + y * orows) * out->ld
+                                        : (static_cast<i128>(g - group_begin) * N + y) * out->block_stride,
                  orows, n};
       if ((st = check_extent(out, d, "out"))) return st;
       RowJob J;
       std::memset(&J, 0, sizeof J);
       J.src = P + src0 + y * orows * partials->ld;
-      J.dst = O + d.offset;
+      J.dst = O + d.off();
       J.src_stride = partials->block_stride;
       J.lds = partials->ld;
       J.ldd = out->ld;
@@ -137,10 +137,11 @@ extern "C" int32_t sm_reshard(const sm_mesh* mesh, const sm_spec* from, const sm
 
   const int64_t esz = static_cast<int64_t>(dtype_size(dtype));
   // Offset (elements) of global element (r, c) inside a buffer laid out by grid g.
-  auto where = [](const sm_buf* b, const Grid& g, int64_t r, int64_t c) -> int64_t {
-    if (b->block_stride == 0) return r * b->ld + c;
+  auto where = [](const sm_buf* b, const Grid& g, int64_t r, int64_t c) -> i128 {
+    if (b->block_stride == 0) return static_cast<i128>(r) * b->ld + c;
     const int64_t bi = r / g.br, bj = c / g.bc;
-    return (bi * g.gc + bj) * b->block_stride + (r - bi * g.br) * b->ld + (c - bj * g.bc);
+    return (static_cast<i128>(bi) * g.gc + bj) * b->block_stride + static_cast<i128>(r - bi * g.br) * b->ld +
+           (c - bj * g.bc);
   };
   std::vector<RowJob> jobs;
   for (int64_t di = 0; di < gd.gr; ++di)
@@ -157,8 +158,8 @@ extern "C" int32_t sm_reshard(const sm_mesh* mesh, const sm_spec* from, const sm
           if ((st = check_extent(dst, d, "dst"))) return st;
           RowJob J;
           std::memset(&J, 0, sizeof J);
-          J.src = static_cast<const char*>(src->ptr) + s.offset * esz;
-          J.dst = static_cast<char*>(dst->ptr) + d.offset * esz;
+          J.src = static_cast<const char*>(src->ptr) + s.off() * esz;
+          J.dst = static_cast<char*>(dst->ptr) + d.off() * esz;
           J.src_stride = 0;
           J.lds = src->ld;
           J.ldd = dst->ld;

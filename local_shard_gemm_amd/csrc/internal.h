@@ -37,9 +37,14 @@ size_t dtype_size(int32_t dt);
 // ---- buffer checks and row-job launches shared by the device entry points
 
 // One logical block of a buffer: element offset of its (0,0) and its extent.
+// Offsets are computed in 128 bits from caller-supplied sizes, so that no
+// product can wrap before check_extent bounds it by the buffer's elems;
+// off() narrows it once the check has passed.
+typedef __int128 i128;
 struct BlockRef {
-  int64_t offset;
+  i128 offset;
   int64_t rows, cols;
+  int64_t off() const { return static_cast<int64_t>(offset); }
 };
 // Pointer, alignment, ld, block_stride and elems of one sm_buf.
 int32_t check_buf_basic(const sm_buf* b, const char* what, int32_t dtype);

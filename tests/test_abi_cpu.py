@@ -379,3 +379,23 @@ def test_empty_inputs_refused():
     assert _err(sm.sm_local_gemm_reduce, p3, A, B, _fb(64), 0, 0, 0) == sm.SM_ERR_ARG
     assert _err(sm.sm_reshard, {"X": 2}, "A[I, J_X]", "A[I_X, J]", 0, 8, sm.SM_F32, _fb(8, 32), _fb(8, 32)) \
         == sm.SM_ERR_SHAPE
+
+
+def test_extent_checks_do_not_wrap():
+    """Offsets and extents are computed without 64-bit wrap: an absurd ld or
+    block_stride (here 2^62) cannot make an out-of-range block look in range."""
+    p1 = sm.sm_plan({"X": 2}, "P('X', None)", "P()", 64, 128, 64)
+    B, C = _fb(64, dt=BF), _fb(64, 32 * 64)
+    huge = 1 << 62
+    # 31 rows of ld 2^62 past a zero offset: 31 * 2^62 wraps negative in 64 bits
+    assert _err(sm.sm_local_gemm, p1, _fb(huge, elems=1 << 40, dt=BF), B, C) == sm.SM_ERR_SHAPE
+    # stacked input: unit 4 reads A block 4 at 4 * 2^62, which wraps to 0 in 64 bits
+    p8 = sm.sm_plan({"X": 8}, "P('X', None)", "P()", 64, 64, 64)
+    assert _err(sm.sm_local_gemm, p8, _fb(64, huge, elems=1 << 40, dt=BF), _fb(64, dt=BF), _fb(64, 8 * 64),
+                sm.SM_EPI_STORE, 4, 1) == sm.SM_ERR_SHAPE
+    p3 = sm.sm_plan({"X": 2}, "P(None, 'X')", "P('X', None)", 8, 16, 8)
+    assert _err(sm.sm_reduce_partials, p3, _fb(8, huge, elems=1 << 40), _fb(8)) == sm.SM_ERR_SHAPE
+    assert _err(sm.sm_gather_shards, p1, sm.SM_WHAT_C_BLOCKS, _fb(64, huge, elems=1 << 40), _fb(64)) \
+        == sm.SM_ERR_SHAPE
+    assert _err(sm.sm_reshard, {"X": 4}, "A[I, J_X]", "A[I_X, J]", 8, 16, sm.SM_F32, _fb(4, huge, elems=1 << 40),
+                _fb(16, 32)) == sm.SM_ERR_SHAPE
