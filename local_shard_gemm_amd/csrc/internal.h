@@ -9,6 +9,7 @@
 namespace shardmm {
 
 constexpr uint32_t kPlanMagic = 0x5348414Du;  // "SHAM"
+constexpr int64_t kMaxRanks = int64_t(1) << 20;  // logical ranks per mesh
 
 // Record a failure and return its status (thread-local text for sm_last_error).
 int32_t fail(int32_t status, const std::string& msg);

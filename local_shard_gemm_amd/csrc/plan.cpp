@@ -56,9 +56,16 @@ static void unflatten(const sm_mesh& mesh, const int32_t* axes, int32_t n, int32
   }
 }
 
+// A plan is trusted only if it is exactly what sm_plan makes of its own
+// inputs (mesh, specs, sizes, dtypes): a plan edited after the fact could
+// otherwise carry zero divisors or shapes that disagree with its views.
 int32_t check_plan(const sm_plan_t* p) {
   if (!p) return fail(SM_ERR_ARG, "plan is NULL");
   if (p->magic != kPlanMagic) return fail(SM_ERR_ARG, "plan was not filled by sm_plan");
+  sm_plan_t q;
+  if (sm_plan(&p->mesh, &p->a, &p->b, p->I, p->J, p->K, p->in_dtype, p->out_dtype, &q) != SM_OK ||
+      std::memcmp(&q, p, sizeof q) != 0)
+    return fail(SM_ERR_ARG, "plan was modified after sm_plan");
   return SM_OK;
 }
 
@@ -341,8 +348,12 @@ int32_t sm_plan(const sm_mesh* mesh, const sm_spec* a, const sm_spec* b, int64_t
   clear_error();
   if (!mesh || !a || !b || !out) return fail(SM_ERR_ARG, "NULL argument");
   if (mesh->n_axes < 1 || mesh->n_axes > SM_MAX_AXES) return fail(SM_ERR_MESH, "1 to 4 axes");
-  for (int32_t x = 0; x < mesh->n_axes; ++x)
+  int64_t ranks = 1;
+  for (int32_t x = 0; x < mesh->n_axes; ++x) {
     if (mesh->sizes[x] < 1) return fail(SM_ERR_MESH, "axis sizes must be >= 1");
+    ranks *= mesh->sizes[x];
+    if (ranks > kMaxRanks) return fail(SM_ERR_MESH, "more than 2^20 ranks");
+  }
   int32_t st;
   if ((st = validate_spec_impl(*mesh, *a, "A"))) return st;
   if ((st = validate_spec_impl(*mesh, *b, "B"))) return st;
@@ -418,7 +429,7 @@ int32_t sm_plan(const sm_mesh* mesh, const sm_spec* a, const sm_spec* b, int64_t
     for (int32_t k = 0; k < a->n[1]; ++k) p.c_rs.axes[0][p.c_rs.n[0]++] = a->axes[1][k];
   }
   p.magic = kPlanMagic;
-  *out = p;
+  std::memcpy(out, &p, sizeof p);  // padding bytes included: check_plan compares bytes
   return SM_OK;
 }
 

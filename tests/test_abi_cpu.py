@@ -399,3 +399,30 @@ def test_extent_checks_do_not_wrap():
         == sm.SM_ERR_SHAPE
     assert _err(sm.sm_reshard, {"X": 4}, "A[I, J_X]", "A[I_X, J]", 8, 16, sm.SM_F32, _fb(4, huge, elems=1 << 40),
                 _fb(16, 32)) == sm.SM_ERR_SHAPE
+
+
+def test_modified_plan_refused():
+    """A plan is used only as sm_plan made it: editing any field afterwards
+    (a zero partial count, a different local shape) is refused before any
+    arithmetic uses it."""
+    p = sm.sm_plan({"X": 2}, "P(None, 'X')", "P('X', None)", 64, 128, 64)
+    A, B, C = _fb(128, dt=BF), _fb(64, dt=BF), _fb(64, 64 * 64)
+    for field, value in (("n_partials", 0), ("n_units", 64), ("kase", sm.SM_CASE1)):
+        q = sm.sm_plan_t.from_buffer_copy(p)
+        setattr(q, field, value)
+        assert _err(sm.sm_local_gemm, q, A, B, C) == sm.SM_ERR_ARG, field
+        assert "modified" in sm.sm_last_error()
+        assert _err(sm.sm_reduce_partials, q, C, _fb(64)) == sm.SM_ERR_ARG, field
+    q = sm.sm_plan_t.from_buffer_copy(p)
+    q.c_local[1] = 32
+    assert _err(sm.sm_gather_shards, q, sm.SM_WHAT_C_BLOCKS, C, _fb(64)) == sm.SM_ERR_ARG
+    # an untouched copy is accepted (it fails only at the launch, with no GPU here)
+    q = sm.sm_plan_t.from_buffer_copy(p)
+    assert _err(sm.sm_local_gemm, q, A, B, C) in (sm.SM_ERR_HIP, sm.SM_ERR_SHAPE)
+
+
+def test_mesh_rank_limit():
+    with pytest.raises(sm.ShardmmError) as ei:
+        sm.sm_plan({"A": 1024, "B": 1025}, "P()", "P()", 8, 8, 8)
+    assert ei.value.status == sm.SM_ERR_MESH
+    assert sm.sm_plan({"A": 1024, "B": 1024}, "P()", "P()", 8, 8, 8).n_ranks == 1 << 20
