@@ -39,6 +39,10 @@
  *    so element counts are never applied to the wrong element size.
  *  - Alignment: base pointers 16-byte aligned; ld and block_stride multiples
  *    of 8 elements for bfloat16 and of 4 for float32 (SM_ERR_ALIGN).
+ *  - Memory: every buffer must be addressable by the GPU (device, managed,
+ *    or HIP-allocated / registered host memory). Pageable host memory is
+ *    refused with SM_ERR_ARG as the last check before a launch. Outputs
+ *    must not overlap inputs.
  */
 #ifndef SHARDMM_H
 #define SHARDMM_H

@@ -58,6 +58,23 @@ int32_t hip_fail(hipError_t e, const char* where) {
   return fail(SM_ERR_HIP, std::string(where) + ": " + hipGetErrorString(e));
 }
 
+// Memory a kernel will touch must be addressable by the GPU: device,
+// managed, or HIP-allocated / registered host memory. A plain host pointer
+// would fault the kernel, so it is refused here, after every other check
+// and before any launch.
+int32_t check_device_memory(const void* ptr, const char* what) {
+  hipPointerAttribute_t attr;
+  const hipError_t e = hipPointerGetAttributes(&attr, ptr);
+  if (e == hipErrorInvalidValue) {
+    (void)hipGetLastError();  // not sticky; keep it out of the launch checks
+    return fail(SM_ERR_ARG, std::string(what) + ": not memory the GPU can address");
+  }
+  if (e != hipSuccess) return hip_fail(e, what);
+  if (attr.type == hipMemoryTypeUnregistered || attr.devicePointer == nullptr)
+    return fail(SM_ERR_ARG, std::string(what) + ": not memory the GPU can address");
+  return SM_OK;
+}
+
 }  // namespace shardmm
 
 using namespace shardmm;
@@ -128,6 +145,9 @@ extern "C" int32_t sm_local_gemm(const sm_plan_t* plan, const sm_buf* A, const s
     it.ptrs.c = static_cast<char*>(C->ptr) + rc.off() * static_cast<int64_t>(csz);
     items.push_back(it);
   }
+  if ((st = check_device_memory(A->ptr, "A")) || (st = check_device_memory(B->ptr, "B")) ||
+      (st = check_device_memory(C->ptr, "C")))
+    return st;
   // Units sharing a B block go next to each other (their tiles stack into
   // one tall matrix in the kernel's tile order).
   std::stable_sort(items.begin(), items.end(), [](const Item& x, const Item& y) {
@@ -272,6 +292,7 @@ extern "C" int32_t sm_reduce_partials(const sm_plan_t* plan, const sm_buf* parti
       jobs.push_back(J);
     }
   }
+  if ((st = check_device_memory(partials->ptr, "partials")) || (st = check_device_memory(out->ptr, "out"))) return st;
   return run_jobs(jobs, N, 4, static_cast<hipStream_t>(stream), "sm_reduce_partials launch");
 }
 
@@ -363,6 +384,7 @@ extern "C" int32_t sm_gather_shards(const sm_plan_t* plan, int32_t what, const s
     J.cols = static_cast<int32_t>(cols);
     jobs.push_back(J);
   }
+  if ((st = check_device_memory(shards->ptr, "shards")) || (st = check_device_memory(out->ptr, "out"))) return st;
   return run_jobs(jobs, 1, static_cast<int32_t>(esz), static_cast<hipStream_t>(stream), "sm_gather_shards launch");
 }
 
@@ -455,6 +477,9 @@ extern "C" int32_t sm_local_gemm_reduce(const sm_plan_t* plan, const sm_buf* A, 
     if (reinterpret_cast<uintptr_t>(it.ptrs.c) % 8) L.vec_c = 0;
     items.push_back(it);
   }
+  if ((st = check_device_memory(A->ptr, "A")) || (st = check_device_memory(B->ptr, "B")) ||
+      (st = check_device_memory(out->ptr, "out")))
+    return st;
   std::stable_sort(items.begin(), items.end(), [](const Item& x, const Item& y) {
     return x.b_id != y.b_id ? x.b_id < y.b_id : x.a_row < y.a_row;
   });

@@ -75,6 +75,9 @@ extern "C" int32_t sm_reduce_scatter_layernorm(const sm_plan_t* plan, const sm_b
       jobs.push_back(J);
     }
   }
+  if ((st = check_device_memory(partials->ptr, "partials")) || (st = check_device_memory(out->ptr, "out")) ||
+      (gamma && (st = check_device_memory(gamma, "gamma"))) || (beta && (st = check_device_memory(beta, "beta"))))
+    return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   RowLaunch L;
   for (size_t first = 0; first < jobs.size(); first += kMaxJobsPerLaunch) {
@@ -174,5 +177,6 @@ extern "C" int32_t sm_reshard(const sm_mesh* mesh, const sm_spec* from, const sm
   // 5.6 TB/s).
   std::stable_sort(jobs.begin(), jobs.end(),
                    [](const RowJob& a, const RowJob& b) { return a.src < b.src; });
+  if ((st = check_device_memory(src->ptr, "src")) || (st = check_device_memory(dst->ptr, "dst"))) return st;
   return run_jobs(jobs, 1, static_cast<int32_t>(esz), static_cast<hipStream_t>(stream), "sm_reshard launch");
 }

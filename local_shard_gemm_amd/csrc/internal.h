@@ -51,6 +51,8 @@ struct BlockRef {
 int32_t check_buf_basic(const sm_buf* b, const char* what, int32_t dtype);
 // The block lies inside the buffer.
 int32_t check_extent(const sm_buf* b, const BlockRef& r, const char* what);
+// The GPU can address the memory at ptr (device, managed or HIP host memory).
+int32_t check_device_memory(const void* ptr, const char* what);
 // Stacked blocks of rows x cols do not overlap.
 int32_t check_stacked(const sm_buf* b, int64_t rows, int64_t cols, const char* what);
 

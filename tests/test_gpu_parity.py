@@ -538,3 +538,34 @@ def test_full_skinny_all_outputs(integer):
         say("skinny partial rel err", worst)
         assert worst <= REL_TOL
         assert ref.rel_frobenius(out.cpu().numpy(), s) <= REL_TOL
+
+
+def test_host_memory_refused_before_launch():
+    """A pageable host buffer (a CPU tensor) handed to a device entry point is
+    refused on the host with SM_ERR_ARG before anything is launched; the
+    device outputs are untouched."""
+    say("case: host memory refused")
+    I, J, K = 64, 128, 64
+    A, B = _int((I, J), 71), _int((J, K), 72)
+    p, q = _plans({"X": 2}, "P(None, 'X')", "P('X', None)", I, J, K)
+    Ad, Bd = to_dev(A), to_dev(B)
+    P = torch.full((2, I, K), float("nan"), device=DEV)
+    for args in ((sm.buf(A), sm.buf(Bd), sm.buf(P)), (sm.buf(Ad), sm.buf(Bd), sm.buf(torch.zeros(2, I, K)))):
+        with pytest.raises(sm.ShardmmError) as ei:
+            sm.sm_local_gemm(p, *args)
+        assert ei.value.status == sm.SM_ERR_ARG and "GPU can address" in str(ei.value)
+    torch.cuda.synchronize()
+    assert bool(torch.isnan(P).all())
+    sm.sm_local_gemm(p, sm.buf(Ad), sm.buf(Bd), sm.buf(P))
+    out = torch.full((I, K), float("nan"), device=DEV)
+    for call in (lambda: sm.sm_reduce_partials(p, sm.buf(P.cpu()), sm.buf(out)),
+                 lambda: sm.sm_gather_shards(p, sm.SM_WHAT_C_SCATTERED, sm.buf(P.cpu()), sm.buf(out)),
+                 lambda: sm.sm_local_gemm_reduce(p, sm.buf(A), sm.buf(Bd), sm.buf(out)),
+                 lambda: sm.sm_reduce_scatter_layernorm(p, sm.buf(P), sm.buf(out), torch.ones(K), None),
+                 lambda: sm.sm_reshard({"X": 2}, "A[I, J_X]", "A[I_X, J]", I, K, sm.SM_F32, sm.buf(out.cpu(), block_stride=0),
+                                       sm.buf(P))):
+        with pytest.raises(sm.ShardmmError) as ei:
+            call()
+        assert ei.value.status == sm.SM_ERR_ARG, ei.value
+    torch.cuda.synchronize()
+    assert bool(torch.isnan(out).all())
