@@ -103,6 +103,8 @@ extern "C" int32_t sm_local_gemm(const sm_plan_t* plan, const sm_buf* A, const s
 
   const int64_t m = p.a_local[0], k = p.a_local[1], n = p.b_local[1];
   if (m > INT32_MAX / 2 || n > INT32_MAX / 2 || k > INT32_MAX / 2) return fail(SM_ERR_SHAPE, "local shape too large");
+  if (((m + kTileM - 1) / kTileM) * ((n + kTileN - 1) / kTileN) * kMaxUnitsPerLaunch > INT32_MAX)
+    return fail(SM_ERR_SHAPE, "too many output tiles for one launch grid");
   if (A->block_stride == 0 && A->ld < p.J) return fail(SM_ERR_SHAPE, "A: global layout needs ld >= J");
   if (B->block_stride == 0 && B->ld < p.K) return fail(SM_ERR_SHAPE, "B: global layout needs ld >= K");
   if (C->block_stride == 0 && C->ld < p.K) return fail(SM_ERR_SHAPE, "C: global layout needs ld >= K");
@@ -412,6 +414,8 @@ extern "C" int32_t sm_local_gemm_reduce(const sm_plan_t* plan, const sm_buf* A, 
   const int32_t N = p.n_partials;
   if (m <= kSkinnyMaxM) return fail(SM_ERR_SHAPE, "skinny products reduce through sm_reduce_partials");
   if (m > INT32_MAX / 2 || n > INT32_MAX / 2 || kfull > INT32_MAX / 2) return fail(SM_ERR_SHAPE, "shape too large");
+  if (((m + kTileM - 1) / kTileM) * ((n + kTileN - 1) / kTileN) * kMaxUnitsPerLaunch > INT32_MAX)
+    return fail(SM_ERR_SHAPE, "too many output tiles for one launch grid");
   const bool rs = mode == SM_REDUCESCATTER;
   if (rs && m % N) return fail(SM_ERR_INDIVISIBLE, "rows of a block do not split N ways");
   const int64_t orows = rs ? m / N : m;

@@ -426,3 +426,16 @@ def test_mesh_rank_limit():
         sm.sm_plan({"A": 1024, "B": 1025}, "P()", "P()", 8, 8, 8)
     assert ei.value.status == sm.SM_ERR_MESH
     assert sm.sm_plan({"A": 1024, "B": 1024}, "P()", "P()", 8, 8, 8).n_ranks == 1 << 20
+
+
+def test_launch_grid_bound():
+    """Local outputs whose tile grid could not be addressed by one launch are
+    refused before any arithmetic on them (a [2^29, 2^29] block)."""
+    p = sm.sm_plan({"X": 1}, "P()", "P()", 1 << 29, 64, 1 << 29)
+    n = 1 << 29
+    assert _err(sm.sm_local_gemm, p, _fb(64, dt=BF), _fb(n, dt=BF), _fb(n, elems=1 << 62)) == sm.SM_ERR_SHAPE
+    assert "tiles" in sm.sm_last_error()
+    pr = sm.sm_plan({"X": 1}, "P(None, 'X')", "P('X', None)", 1 << 29, 64, 1 << 29)
+    assert _err(sm.sm_local_gemm_reduce, pr, _fb(64, dt=BF), _fb(n, dt=BF), _fb(n, elems=1 << 62),
+                sm.SM_ALLREDUCE) == sm.SM_ERR_SHAPE
+    assert "tiles" in sm.sm_last_error()
