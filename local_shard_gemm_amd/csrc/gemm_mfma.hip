@@ -35,6 +35,8 @@
 //    so their tiles stack into one tall virtual matrix.
 #include "kernels.h"
 
+#include <type_traits>
+
 namespace shardmm {
 namespace {
 
@@ -301,11 +303,14 @@ __device__ __forceinline__ void run_tile(const GemmLaunch& L, const uint16_t* __
 // ---------------------------------------------------------------------------
 // Interior tiles: direct HBM -> LDS pipeline.
 //
-//  * Both operands travel global -> LDS with global_load_lds_dwordx4 (16
+//  * Both operands travel global -> LDS with buffer_load_dwordx4 ... lds (16
 //    bytes per lane, landing at M0 + 16 * lane): no staging registers, no
-//    LDS stores, no register transpose.
-//  * K advances 32 at a time through 4 LDS stages of 32 KiB (A 256x32, B
-//    32x256); loads run 3 stages ahead of the matrix cores.
+//    LDS stores, no register transpose. Each lane's byte offset inside the
+//    tile is fixed; the k advance moves the buffer resource's base (scalar
+//    arithmetic), so a load costs no vector instructions.
+//  * K advances 32 at a time through a ring of 5 LDS stages of 32 KiB (A
+//    256x32, B 32x256; 160 KiB, the whole LDS); loads run 3 stages ahead of
+//    the stage being read.
 //  * A stage: row r holds 32 k (64 bytes = 4 chunks); chunk c of row r sits
 //    at c ^ ((r >> 2) & 3). A fragments are 16-byte LDS reads (8 k of one
 //    row per lane).
@@ -317,12 +322,14 @@ __device__ __forceinline__ void run_tile(const GemmLaunch& L, const uint16_t* __
 //    give a lane the 8 k values of its column.
 //  * Both swizzles make every fragment read touch each LDS bank the minimum
 //    number of times.
-//  * Fragments for the next 16-k step are read while the current step's 16
-//    MFMAs run; the first step of a stage overlaps the previous stage's last
-//    MFMAs (issued after the barrier).
+//  * Three fragment sets: the fragments of k16 step t+2 are read while the
+//    MFMAs of step t run, so an LDS read has two steps (32 MFMAs) to land
+//    instead of one. With two sets the waves spent about a quarter of their
+//    time waiting on fragment reads that the stage's DMA traffic had
+//    delayed.
 // ---------------------------------------------------------------------------
 constexpr int BK2 = 32;
-constexpr int STAGES = 4;
+constexpr int STAGES = 5;
 constexpr int A_STAGE = BM * BK2 * 2;  // bytes
 constexpr int B_STAGE = BK2 * BN * 2;
 constexpr int STAGE_BYTES = A_STAGE + B_STAGE;
@@ -334,15 +341,12 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
-// s_waitcnt with only vmcnt = n (expcnt and lgkmcnt left unconstrained).
-template <int n>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(n >= 0 && n < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((n & 0xF) | ((n >> 4) << 14) | 0x70 | 0xF00);
+// s_waitcnt vmcnt(vm) lgkmcnt(lg) (expcnt unconstrained).
+template <int vm, int lg>
+__device__ __forceinline__ void wait_cnt() {
+  static_assert(vm >= 0 && vm < 64 && lg >= 0 && lg < 16, "waitcnt range");
+  __builtin_amdgcn_s_waitcnt((vm & 0xF) | ((vm >> 4) << 14) | 0x70 | (lg << 8));
 }
-
-// s_waitcnt lgkmcnt(0) only (vmcnt left at its maximum, 63).
-__device__ __forceinline__ void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(0xF | (3 << 14) | 0x70); }
 
 struct Frags {
   bf16x8 a[4];
@@ -353,37 +357,29 @@ template <bool OUT_BF16, bool GELU>
 __device__ __forceinline__ void run_tile_lds(const GemmLaunch& L, const uint16_t* __restrict__ A,
                                              const uint16_t* __restrict__ B, void* C, int row0, int col0,
                                              lds_char* smem) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
   const int64_t lda = L.lda, ldb = L.ldb;
 
-  // ---- loader: each wave fills 4 KiB of A and 4 KiB of B per stage, 1 KiB
-  // per instruction. A: rows (4w+i)*16 + lane/4, physical chunk lane%4;
-  // B: rows (4w+i)*2 + lane/32, physical chunk lane%32.
-  const uint16_t* ga[4];
-  const uint16_t* gb[4];
+  // ---- loader: per wave and stage 4 A items (rows (4w+i)*16 + lane/4,
+  // 64 bytes each) and 4 B items (rows (4w+i)*2 + lane/32, 512 bytes each),
+  // 1 KiB per instruction, through buffer loads whose per-lane offsets stay
+  // fixed; the k advance moves the resource base.
+  int va[4], vb[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int ra = (4 * wave + i) * 16 + (lane >> 2);
     const int ca = (lane & 3) ^ ((ra >> 2) & 3);
-    ga[i] = A + static_cast<int64_t>(row0 + ra) * lda + 8 * ca;
+    va[i] = static_cast<int>((static_cast<int64_t>(ra) * lda + 8 * ca) * 2);
     const int rb = (4 * wave + i) * 2 + (lane >> 5);
     const int cb = (lane & 31) ^ ((rb & 3) << 2);
-    gb[i] = B + static_cast<int64_t>(rb) * ldb + col0 + 8 * cb;
+    vb[i] = static_cast<int>((static_cast<int64_t>(rb) * ldb + 8 * cb) * 2);
   }
-  auto issue = [&](int kt) {
-    lds_char* st = smem + (kt % STAGES) * STAGE_BYTES;
-    const int64_t ka = static_cast<int64_t>(kt) * BK2;
-    const int64_t kb = ka * ldb;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      __builtin_amdgcn_global_load_lds(ga[i] + ka, (lds_void*)(st + (4 * wave + i) * 1024), 16, 0, 0);
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      __builtin_amdgcn_global_load_lds(gb[i] + kb, (lds_void*)(st + A_STAGE + (4 * wave + i) * 1024), 16, 0, 0);
-  };
+  const char* a_tile = reinterpret_cast<const char*>(A + static_cast<int64_t>(row0) * lda);
+  const char* b_tile = reinterpret_cast<const char*>(B + col0);
+  const int64_t a_step = BK2 * 2, b_step = static_cast<int64_t>(BK2) * ldb * 2;
 
-  // ---- fragment addresses (byte offsets inside a stage)
   int a_off[2][4];
   int b_off[2][4][2];
 #pragma unroll
@@ -405,67 +401,8 @@ __device__ __forceinline__ void run_tile_lds(const GemmLaunch& L, const uint16_t
         b_off[s][ni][t] = A_STAGE + kr * (BN * 2) + ((ch ^ ((kr & 3) << 2)) << 4) + half * 8;
       }
   }
-  auto read_frags = [&](Frags& F, int kt, int s) {
-    lds_char* st = smem + (kt % STAGES) * STAGE_BYTES;
-#pragma unroll
-    for (int mi = 0; mi < 4; ++mi)
-      F.a[mi] = __builtin_bit_cast(bf16x8, *(lds_u4*)(st + a_off[s][mi]));
-#pragma unroll
-    for (int ni = 0; ni < 4; ++ni) {
-      const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(st + b_off[s][ni][0]));
-      const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(st + b_off[s][ni][1]));
-      F.b[ni] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-    }
-  };
-
-  f32x16 acc[4][4];
-#pragma unroll
-  for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-    for (int ni = 0; ni < 4; ++ni)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[mi][ni][v] = 0.0f;
-  auto mma = [&](const Frags& F) {
-#pragma unroll
-    for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-      for (int ni = 0; ni < 4; ++ni)
-        acc[mi][ni] = mfma_block<OUT_BF16>(F.a[mi], F.b[ni], acc[mi][ni]);
-  };
-
-  const int nk = L.K / BK2;
-  // prologue: stages 0..2 in flight
-#pragma unroll
-  for (int p = 0; p < STAGES - 1; ++p)
-    if (p < nk) issue(p);
-
-  // F1 starts as zeros so that every iteration has the same straight-line
-  // body (its first MFMA step adds exact zeros).
-  Frags F0, F1;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    F1.a[i] = bf16x8{};
-    F1.b[i] = bf16x8{};
-  }
-  // Own LDS reads finished (the buffer refilled next was read last step),
-  // then a bare barrier: a full __syncthreads() fence would also wait for
-  // the loads still in flight for later stages.
-  auto stage_barrier = [&]() {
-    wait_lgkmcnt0();
-    asm volatile("" ::: "memory");  // keep LDS reads and DMA issues on their side
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-  };
-
-  // Steady state: the body is one straight-line block so the scheduler can
-  // interleave. Per stage and wave: 8 DMA loads (stage kt+3), 24 fragment
-  // reads and 32 MFMAs. Each half: 12 fragment reads in the shadow of the
-  // first 6 MFMAs, 4 DMA loads in the shadow of the next 4, then 6 MFMAs;
-  // spreading the DMA keeps the 4 waves from queueing on the address unit
-  // right after the barrier.
-  // One fragment-read item (0..11): A fragments 0..3, then the two
-  // transposing halves of B fragments 0..3.
-  auto read_item = [&](Frags& F, lds_char* st, int s, int item) {
+  auto read_item = [&](Frags& F, int sb, int s, int item) {
+    lds_char* st = smem + sb;
     if (item < 4) {
       F.a[item] = __builtin_bit_cast(bf16x8, *(lds_u4*)(st + a_off[s][item]));
     } else {
@@ -477,67 +414,105 @@ __device__ __forceinline__ void run_tile_lds(const GemmLaunch& L, const uint16_t
         F.b[ni] = __builtin_shufflevector(F.b[ni].lo, v, 0, 1, 2, 3, 4, 5, 6, 7);
     }
   };
-  // One DMA item (0..7): A rows for 0..3, B rows for 4..7.
-  auto dma_item = [&](int kt_load, int item) {
-    lds_char* st = smem + (kt_load % STAGES) * STAGE_BYTES;
-    const int64_t ka = static_cast<int64_t>(kt_load) * BK2;
-    if (item < 4)
-      __builtin_amdgcn_global_load_lds(ga[item] + ka, (lds_void*)(st + (4 * wave + item) * 1024), 16, 0, 0);
-    else
-      __builtin_amdgcn_global_load_lds(gb[item - 4] + ka * ldb,
-                                       (lds_void*)(st + A_STAGE + (4 * wave + item - 4) * 1024), 16, 0, 0);
+  // DMA item of stage kt_load into the stage buffer at byte offset sb.
+  auto dma_item = [&](int kt_load, int sb, int item) {
+    if (item < 4) {
+      const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)(a_tile + kt_load * a_step), (short)0, 0x7fffffff, 0x00020000);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(smem + sb + (4 * wave + item) * 1024), 16, va[item], 0, 0, 0);
+    } else {
+      const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)(b_tile + kt_load * b_step), (short)0, 0x7fffffff, 0x00020000);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(smem + sb + A_STAGE + (4 * wave + item - 4) * 1024), 16,
+                                               vb[item - 4], 0, 0, 0);
+    }
   };
-  // Half a stage in fixed program order: 16 MFMAs on `cur`; the 12
-  // fragment reads of `nxt` ride on the first 6, and DMA items
-  // [dma0, dma0+4) (if any) on MFMAs 3, 7, 11 and 15 -- one DMA per four
-  // MFMAs per wave keeps the address unit below saturation with 4 waves.
-  // sched_barrier(0) pins the order.
-  auto half = [&](const Frags& cur, Frags& nxt, lds_char* st_next, int s_next, int kt_load, int dma0) {
+
+  f32x16 acc[4][4];
+#pragma unroll
+  for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < 4; ++ni)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[mi][ni][v] = 0.0f;
+
+  // One k16 step: 16 MFMAs on `cur`; the 12 fragment reads of the step two
+  // ahead ride one per MFMA on the first 12 (if rd), DMA items
+  // [dma0, dma0 + 4) on MFMAs 3, 7, 11, 15 (if ld).
+  auto step = [&](const Frags& cur, Frags& nxt, bool rd, int sb_rd, int s_rd, bool ld, int kt_load, int sb_ld,
+                  int dma0) {
 #pragma unroll
     for (int idx = 0; idx < 16; ++idx) {
       const int mi = idx >> 2, ni = idx & 3;
       acc[mi][ni] = mfma_block<OUT_BF16>(cur.a[mi], cur.b[ni], acc[mi][ni]);
-      if (idx < 6) {
-        read_item(nxt, st_next, s_next, 2 * idx);
-        read_item(nxt, st_next, s_next, 2 * idx + 1);
-      }
-      if ((idx & 3) == 3 && dma0 >= 0) dma_item(kt_load, dma0 + (idx >> 2));
+      if (idx < 12 && rd) read_item(nxt, sb_rd, s_rd, idx);
+      if ((idx & 3) == 3 && ld) dma_item(kt_load, sb_ld, dma0 + (idx >> 2));
       __builtin_amdgcn_sched_barrier(0);
     }
   };
 
-  int kt = 0;
-  for (; kt + STAGES - 1 < nk; ++kt) {
-    wait_vmcnt<16>();  // this wave's loads of stage kt have landed
-    stage_barrier();   // ... and every wave's; buffer of stage kt-1 is free
-    lds_char* st = smem + (kt % STAGES) * STAGE_BYTES;
-    half(F1, F0, st, 0, kt + STAGES - 1, 0);  // previous stage's last step; A loads of stage kt+3
-    half(F0, F1, st, 1, kt + STAGES - 1, 4);  // B loads of stage kt+3
-  }
-  // Last stages: nothing left to load.
-  for (; kt < nk; ++kt) {
-    if (kt + 2 < nk)
-      wait_vmcnt<16>();
-    else if (kt + 1 < nk)
-      wait_vmcnt<8>();
-    else
-      wait_vmcnt<0>();
-    stage_barrier();
-    read_frags(F0, kt, 0);
-    mma(F1);
-    read_frags(F1, kt, 1);
-    mma(F0);
+  const int nk = L.K / BK2;
+  constexpr int RING = STAGES * STAGE_BYTES;
+  Frags F[3];
+  // prologue: stages 0..3 in flight, then stage 0's fragments
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
+  for (int p = 0; p < STAGES - 1; ++p)
+    if (p < nk) {
 #pragma unroll
-      for (int i = 0; i < 6; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-      }
-      __builtin_amdgcn_sched_group_barrier(0x008, 10, 0);
+      for (int it = 0; it < 8; ++it) dma_item(p, p * STAGE_BYTES, it);
     }
+  if (nk > 3) wait_cnt<24, 15>();
+  else if (nk == 3) wait_cnt<16, 15>();
+  else if (nk == 2) wait_cnt<8, 15>();
+  else wait_cnt<0, 15>();
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+#pragma unroll
+  for (int i = 0; i < 12; ++i) read_item(F[0], 0, 0, i);
+#pragma unroll
+  for (int i = 0; i < 12; ++i) read_item(F[1], 0, 1, i);
+
+  int sb_rd = STAGE_BYTES;                    // buffer of stage kt+1
+  int sb_ld = (STAGES - 1) * STAGE_BYTES;     // buffer of stage kt+4
+  // Iteration kt: steps 2kt and 2kt+1 on F[(2kt)%3], F[(2kt+1)%3]; stage
+  // kt+1's fragments into the other two sets; stage kt+4 into the buffer
+  // stage kt-1 used.
+  auto iter = [&](auto phase_c, int kt, bool steady) {
+    constexpr int P = decltype(phase_c)::value;  // (2kt) % 3
+    constexpr int P0 = P, P1 = (P + 1) % 3, P2 = (P + 2) % 3;
+    const bool rd = steady || kt + 1 < nk;
+    const bool ld = steady || kt + STAGES - 1 < nk;
+    __builtin_amdgcn_sched_barrier(0);
+    if (steady || kt + STAGES - 2 < nk)
+      wait_cnt<16, 12>();
+    else
+      wait_cnt<0, 12>();
+    asm volatile("" ::: "memory");
+    if (rd) __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+    step(F[P0], F[P2], rd, sb_rd, 0, ld, kt + STAGES - 1, sb_ld, 0);
+    if (rd)
+      wait_cnt<63, 12>();
+    else
+      wait_cnt<63, 0>();
+    __builtin_amdgcn_sched_barrier(0);
+    step(F[P1], F[P0], rd, sb_rd, 1, ld, kt + STAGES - 1, sb_ld, 4);
+    sb_rd = sb_rd + STAGE_BYTES == RING ? 0 : sb_rd + STAGE_BYTES;
+    sb_ld = sb_ld + STAGE_BYTES == RING ? 0 : sb_ld + STAGE_BYTES;
+  };
+
+  int kt = 0;
+  for (; kt + 2 + STAGES - 1 < nk; kt += 3) {
+    iter(std::integral_constant<int, 0>{}, kt, true);
+    iter(std::integral_constant<int, 2>{}, kt + 1, true);
+    iter(std::integral_constant<int, 1>{}, kt + 2, true);
   }
-  mma(F1);
+  for (; kt < nk; kt += 3) {
+    iter(std::integral_constant<int, 0>{}, kt, false);
+    if (kt + 1 < nk) iter(std::integral_constant<int, 2>{}, kt + 1, false);
+    if (kt + 2 < nk) iter(std::integral_constant<int, 1>{}, kt + 2, false);
+  }
 
   store_tile<OUT_BF16, GELU, false>(acc, C, L, row0, col0);
 }
@@ -560,10 +535,13 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16_mfma_kernel(const GemmLaunch 
   run_tile_lds<OUT_BF16, GELU>(L, U.a, U.b, U.c, row0, col0, (lds_char*)smem);
 }
 
-// Every tile goes to the edge kernel when K is not a multiple of 32 or a
-// view is not 16-byte aligned.
+// Every tile goes to the edge kernel when K is not a multiple of 32, a view
+// is not 16-byte aligned, or a lane's byte offset inside a tile's buffer
+// resource (up to 255 rows of A, 31 rows of B) would not fit in 31 bits.
 __host__ __device__ __forceinline__ bool all_tiles_edge(const GemmLaunch& L) {
-  return (L.K % BK2) != 0 || !L.vec_ok;
+  constexpr int64_t kMaxOffset = int64_t{1} << 31;
+  return (L.K % BK2) != 0 || !L.vec_ok || (static_cast<int64_t>(BM - 1) * L.lda + BK2) * 2 >= kMaxOffset ||
+         (static_cast<int64_t>(BK2 - 1) * L.ldb + BN) * 2 >= kMaxOffset;
 }
 
 // Edge tiles: the last tile row (M % BM), the last tile column (N % BN), or
