@@ -204,6 +204,70 @@ __device__ __forceinline__ void store_tile(const f32x16 (&acc)[4][4], void* C, c
   }
 }
 
+// Epilogue of an interior tile. The tile lies inside one output block (the
+// host sends launches whose row split would cut a tile to the edge kernel),
+// so every store address is a wave-uniform row base plus a per-lane offset
+// fixed for the whole tile: each store is one instruction with a scalar base
+// and an immediate column offset, and the row arithmetic is scalar. Register
+// layouts as in store_tile.
+template <bool OUT_BF16, bool GELU>
+__device__ __forceinline__ void store_tile_interior(const f32x16 (&acc)[4][4], void* C, const GemmLaunch& L,
+                                                    int row0, int col0, int wave) {
+  const int lane = threadIdx.x & 63;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int64_t ldc = L.ldc;
+  int64_t base;
+  if (L.split_rows < L.M) {
+    const int blk = row0 / L.split_rows;
+    base = blk * L.split_stride + static_cast<int64_t>(row0 - blk * L.split_rows) * ldc;
+  } else {
+    base = static_cast<int64_t>(row0) * ldc;
+  }
+  base += static_cast<int64_t>(wm * 128) * ldc + col0 + wn * 128;
+  if constexpr (!OUT_BF16) {
+    float* cw = static_cast<float*>(C) + base;
+    const int voff = (lane >> 5) * 4 * static_cast<int>(ldc) + (lane & 31);
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        float* rowp = cw + static_cast<int64_t>(mi * 32 + 8 * (v >> 2) + (v & 3)) * ldc;
+#pragma unroll
+        for (int ni = 0; ni < 4; ++ni) {
+          float x = acc[mi][ni][v];
+          if (GELU) x = gelu_tanh_f32(x);
+          rowp[voff + ni * 32] = x;
+        }
+      }
+  } else {
+    uint16_t* cw = static_cast<uint16_t*>(C) + base;
+    const int voff = (lane & 31) * static_cast<int>(ldc) + 4 * (lane >> 5);
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi) {
+      uint16_t* rowp = cw + static_cast<int64_t>(mi * 32) * ldc;
+#pragma unroll
+      for (int ni = 0; ni < 4; ++ni)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          uint32_t h[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            float x = acc[mi][ni][4 * g + e];
+            if (GELU) x = gelu_tanh_f32(x);
+            h[e] = bf16_rne(x);
+          }
+          uint16_t* dst = rowp + voff + ni * 32 + 8 * g;
+          if (L.vec_c) {
+            *reinterpret_cast<uint2*>(dst) = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) dst[e] = static_cast<uint16_t>(h[e]);
+          }
+        }
+    }
+  }
+}
+
 template <bool EDGE, bool OUT_BF16, bool GELU>
 __device__ __forceinline__ void run_tile(const GemmLaunch& L, const uint16_t* __restrict__ A,
                                          const uint16_t* __restrict__ B, void* C, int row0, int col0,
@@ -514,7 +578,7 @@ __device__ __forceinline__ void run_tile_lds(const GemmLaunch& L, const uint16_t
     if (kt + 2 < nk) iter(std::integral_constant<int, 1>{}, kt + 2, false);
   }
 
-  store_tile<OUT_BF16, GELU, false>(acc, C, L, row0, col0);
+  store_tile_interior<OUT_BF16, GELU>(acc, C, L, row0, col0, wave);
 }
 
 // Interior tiles: every tile of the launch is a full BM x BN tile, K is a
@@ -536,12 +600,15 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16_mfma_kernel(const GemmLaunch 
 }
 
 // Every tile goes to the edge kernel when K is not a multiple of 32, a view
-// is not 16-byte aligned, or a lane's byte offset inside a tile's buffer
-// resource (up to 255 rows of A, 31 rows of B) would not fit in 31 bits.
+// is not 16-byte aligned, a lane's byte offset inside a tile's buffer
+// resource (up to 255 rows of A, 31 rows of B) or a lane's element offset
+// inside an output tile (31 rows of C) would not fit in 31 bits, or a row
+// split of the output does not fall on tile boundaries.
 __host__ __device__ __forceinline__ bool all_tiles_edge(const GemmLaunch& L) {
   constexpr int64_t kMaxOffset = int64_t{1} << 31;
   return (L.K % BK2) != 0 || !L.vec_ok || (static_cast<int64_t>(BM - 1) * L.lda + BK2) * 2 >= kMaxOffset ||
-         (static_cast<int64_t>(BK2 - 1) * L.ldb + BN) * 2 >= kMaxOffset;
+         (static_cast<int64_t>(BK2 - 1) * L.ldb + BN) * 2 >= kMaxOffset || L.ldc * 32 >= kMaxOffset ||
+         (L.split_rows < L.M && L.split_rows % BM != 0);
 }
 
 // Edge tiles: the last tile row (M % BM), the last tile column (N % BN), or
