@@ -33,6 +33,7 @@
 //    and the 8 XCDs together cover a 16x16 block through the MALL.
 //  * Units that share a B block are listed next to each other by the host,
 //    so their tiles stack into one tall virtual matrix.
+#include "device_math.h"
 #include "kernels.h"
 
 #include <type_traits>
@@ -85,27 +86,6 @@ __device__ __forceinline__ void transpose8(const uint4 (&in)[8], uint4 (&out)[8]
   }
 }
 
-// GeLU, tanh form: 0.5 x (1 + tanh(z)), z = sqrt(2/pi) (x + 0.044715 x^3),
-// evaluated as x / (1 + exp(-2 z)) -- the same function (1 + tanh(z) =
-// 2 / (1 + exp(-2z))) without the float32 cancellation of 1 + tanh(z) for
-// negative z. exp(-2z) = 2^(-2z log2(e)) on the hardware exp2, and the
-// division as a hardware reciprocal: each adds about one float32 ulp, far
-// below the bfloat16 rounding of the stored H.
-__device__ __forceinline__ float gelu_tanh_f32(float x) {
-  const float k0 = 0.7978845608028654f;  // sqrt(2/pi)
-  const float k1 = 0.044715f;
-  const float m2log2e = -2.0f * 1.4426950408889634f;
-  const float z = k0 * (x + k1 * x * x * x);
-  return x * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(m2log2e * z));
-}
-
-// float -> bfloat16, round to nearest even (NaN stays NaN).
-__device__ __forceinline__ uint16_t bf16_rne(float x) {
-  uint32_t u = __float_as_uint(x);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return static_cast<uint16_t>(u >> 16);
-}
 
 // Workgroup id -> (virtual tile row, tile column). A bijection on [0, T).
 __device__ __forceinline__ void tile_of(int w, int T, int VR, int VC, int* vr, int* vc) {
@@ -249,19 +229,21 @@ __device__ __forceinline__ void store_tile_interior(const f32x16 (&acc)[4][4], v
       for (int ni = 0; ni < 4; ++ni)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          uint32_t h[4];
+          float x[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            float x = acc[mi][ni][4 * g + e];
-            if (GELU) x = gelu_tanh_f32(x);
-            h[e] = bf16_rne(x);
+            x[e] = acc[mi][ni][4 * g + e];
+            if (GELU) x[e] = gelu_tanh_f32(x[e]);
           }
+          const uint32_t p01 = bf16x2_rne(x[0], x[1]), p23 = bf16x2_rne(x[2], x[3]);
           uint16_t* dst = rowp + voff + ni * 32 + 8 * g;
           if (L.vec_c) {
-            *reinterpret_cast<uint2*>(dst) = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
+            *reinterpret_cast<uint2*>(dst) = make_uint2(p01, p23);
           } else {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) dst[e] = static_cast<uint16_t>(h[e]);
+            dst[0] = static_cast<uint16_t>(p01);
+            dst[1] = static_cast<uint16_t>(p01 >> 16);
+            dst[2] = static_cast<uint16_t>(p23);
+            dst[3] = static_cast<uint16_t>(p23 >> 16);
           }
         }
     }

@@ -23,6 +23,7 @@
 //  * The next step's 8 loads are in flight while a step's MFMAs run.
 //  * The 4 wave partials are added in LDS in wave order (a fixed order, so
 //    the result is deterministic) and stored once.
+#include "device_math.h"
 #include "kernels.h"
 
 namespace shardmm {
@@ -76,23 +77,6 @@ __device__ __forceinline__ void transpose8(const uint4 (&in)[8], uint4 (&out)[8]
   }
 }
 
-// GeLU, tanh form, evaluated exactly as in the MFMA GEMM's epilogue:
-// x / (1 + exp(-2z)) with z = sqrt(2/pi) (x + 0.044715 x^3), the exponential
-// on the hardware exp2 and the division as a hardware reciprocal.
-__device__ __forceinline__ float gelu_tanh_f32(float x) {
-  const float k0 = 0.7978845608028654f;  // sqrt(2/pi)
-  const float k1 = 0.044715f;
-  const float m2log2e = -2.0f * 1.4426950408889634f;
-  const float z = k0 * (x + k1 * x * x * x);
-  return x * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(m2log2e * z));
-}
-
-__device__ __forceinline__ uint16_t bf16_rne(float x) {
-  uint32_t u = __float_as_uint(x);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return static_cast<uint16_t>(u >> 16);
-}
 
 struct StepRegs {
   uint4 x;      // X fragment
