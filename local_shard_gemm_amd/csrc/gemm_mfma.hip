@@ -7,8 +7,9 @@
 // Two kernels share the 256x256 output tile per workgroup of 4 waves (2x2),
 // each wave owning a 128x128 sub-tile = 4x4 MFMA blocks of
 // v_mfma_f32_32x32x16_bf16 (256 fp32 accumulators per lane):
-//  * gemm_bf16_mfma_kernel (interior tiles): direct HBM -> LDS loads and
-//    transposing LDS reads, a 4-stage pipeline; described above run_tile_lds.
+//  * gemm_bf16_mfma_kernel (interior tiles): direct HBM -> LDS buffer loads,
+//    transposing LDS reads, a 5-stage LDS ring and three register fragment
+//    sets; described above run_tile_lds.
 //  * gemm_bf16_mfma_edge_kernel (ragged M/N/K, unaligned views): guarded
 //    loads through registers, described here.
 //
