@@ -55,3 +55,21 @@ def test_traffic_record_with_missing_source_is_ignored(fake_root):
     (fake_root / "profiles" / "k_w_counters.md").write_text(_record(fake_root, "gemm", "w", 5))
     os.remove(fake_root / "k.h")
     assert bench.recorded_traffic("gemm", "w") is None
+
+
+def test_rate_hbm_prefers_the_cache_cold_figure():
+    """For an HBM-bound launch whose data would fit in the Infinity Cache the
+    figure is the one measured over rotating buffer copies; the same-buffer
+    (warm) rate is kept apart. Without a cold figure the back-to-back one is
+    reported as is."""
+    import bench
+
+    r = bench.rate("hbm", 8e9, 2.0, cold_ms=4.0)
+    assert r["achieved"] == 2000.0 and r["frac"] == 0.25 and r["avg_ms"] == 4.0
+    assert r["warm_achieved"] == 4000.0 and r["warm_avg_ms"] == 2.0
+    assert r["cache"] == "rotating copies"
+    w = bench.rate("hbm", 8e9, 2.0)
+    assert w["achieved"] == 4000.0 and "warm_achieved" not in w
+    assert w["cache"] == "footprint over 512 MiB"
+    g = bench.rate("mfma", 2.5166e15, 1000.0)
+    assert g["achieved"] == 2516.6 and g["frac"] == 1.0
