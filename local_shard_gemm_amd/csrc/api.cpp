@@ -227,6 +227,11 @@ int32_t run_jobs(std::vector<RowJob>& jobs, int32_t n_sum, int32_t elem_bytes, h
     L.chunk = static_cast<int32_t>(chunk);
     L.n_chunks = static_cast<int32_t>((max_cols + chunk - 1) / chunk);
     if (static_cast<int64_t>(L.max_rows) * L.n_chunks > INT32_MAX) return fail(SM_ERR_SHAPE, "too many rows");
+    // Copies of short rows: 16 KiB of rows per workgroup.
+    const int64_t row_bytes = static_cast<int64_t>(max_cols) * elem_bytes;
+    L.tile_rows = 1;
+    if (n_sum == 1 && L.n_chunks == 1 && row_bytes <= 4096)
+      L.tile_rows = static_cast<int32_t>(std::min<int64_t>(16384 / row_bytes, L.max_rows));
     hipError_t e = launch_rows(L, s);
     if (e != hipSuccess) return hip_fail(e, where);
   }

@@ -53,8 +53,9 @@ struct RowLaunch {
   int32_t n_sum;       // N (1 = plain copy)
   int32_t elem_bytes;  // 4 (float32 sum / copy) or 2 (bfloat16 copy)
   int32_t max_rows;
-  int32_t chunk;     // columns per workgroup (a multiple of 8)
-  int32_t n_chunks;  // column chunks per row
+  int32_t chunk;      // columns per workgroup (a multiple of 8)
+  int32_t n_chunks;   // column chunks per row
+  int32_t tile_rows;  // copies (n_sum 1) of short rows: rows per workgroup (1 = one row each)
   RowJob jobs[kMaxJobsPerLaunch];
 };
 

@@ -45,10 +45,16 @@ __device__ __forceinline__ void add4(float4& a, const float4& b) {
   a.w += b.w;
 }
 
+__device__ __forceinline__ float4 ld4(const float4* p) { return *p; }
+__device__ __forceinline__ void st4(float4* p, const float4& v) { *p = v; }
+
 // Rank-ordered sum of NS partials (NS > 0 fixed at compile time, or the
-// runtime count when NS == 0) for one row, float4 path.
+// runtime count when NS == 0) for one row, float4 path. Sums use
+// non-temporal loads and stores (+40 % over plain ones); a plain copy (NS
+// == 1) measured 5 % faster with plain ones on 8 KiB rows.
 template <int NS>
 __device__ __forceinline__ void sum_row_vec(const RowJob& J, int n_sum, int row) {
+  constexpr bool kNT = NS != 1;
   const int nsum = NS > 0 ? NS : n_sum;
   const float* src = static_cast<const float*>(J.src) + static_cast<int64_t>(row) * J.lds;
   float* dst = static_cast<float*>(J.dst) + static_cast<int64_t>(row) * J.ldd;
@@ -62,8 +68,10 @@ __device__ __forceinline__ void sum_row_vec(const RowJob& J, int n_sum, int row)
 #pragma unroll
         for (int u = 0; u < UNROLL; ++u) {
           const int c4 = base + u * NT;
-          if (c4 < n4)
-            v[y][u] = ldnt(reinterpret_cast<const float4*>(src + y * J.src_stride) + c4);
+          if (c4 < n4) {
+            const float4* q = reinterpret_cast<const float4*>(src + y * J.src_stride) + c4;
+            v[y][u] = kNT ? ldnt(q) : ld4(q);
+          }
         }
 #pragma unroll
       for (int u = 0; u < UNROLL; ++u) {
@@ -88,7 +96,12 @@ __device__ __forceinline__ void sum_row_vec(const RowJob& J, int n_sum, int row)
 #pragma unroll
     for (int u = 0; u < UNROLL; ++u) {
       const int c4 = base + u * NT;
-      if (c4 < n4) stnt(reinterpret_cast<float4*>(dst) + c4, acc[u]);
+      if (c4 < n4) {
+        if (kNT)
+          stnt(reinterpret_cast<float4*>(dst) + c4, acc[u]);
+        else
+          st4(reinterpret_cast<float4*>(dst) + c4, acc[u]);
+      }
     }
   }
 }
@@ -151,6 +164,57 @@ __global__ __launch_bounds__(NT) void rows_b16_copy_kernel(const RowLaunch L) {
     copy_row_16(J, row);
   else
     copy_row_16_scalar(J, row);
+}
+
+// Copy of short rows (at most 4 KiB each): one workgroup per tile of
+// L.tile_rows consecutive rows of a job, walked as one flat sequence of
+// 16-byte vectors; each thread issues all of its CU loads (non-temporal)
+// before its stores. With one 2 KiB row per workgroup half the threads
+// idle and the launch needs 8x as many workgroups: a bf16 gather of
+// [4096,1024] column blocks measured 11.9 us against 12.8 us, from HBM.
+constexpr int CU = 8;
+typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+
+template <int ESZ>
+__global__ __launch_bounds__(NT) void rows_copy_tiled_kernel(const RowLaunch L) {
+  const RowJob J = L.jobs[blockIdx.y];
+  const int r0 = blockIdx.x * L.tile_rows;
+  if (r0 >= J.rows) return;
+  const int rows = min(L.tile_rows, J.rows - r0);
+  const char* src = static_cast<const char*>(J.src) + static_cast<int64_t>(r0) * J.lds * ESZ;
+  char* dst = static_cast<char*>(J.dst) + static_cast<int64_t>(r0) * J.ldd * ESZ;
+  if (!J.vec) {
+    for (int r = 0; r < rows; ++r)
+      for (int c = threadIdx.x; c < J.cols; c += NT) {
+        const int64_t so = (static_cast<int64_t>(r) * J.lds + c) * ESZ, d = (static_cast<int64_t>(r) * J.ldd + c) * ESZ;
+        if (ESZ == 2)
+          *reinterpret_cast<uint16_t*>(dst + d) = *reinterpret_cast<const uint16_t*>(src + so);
+        else
+          *reinterpret_cast<uint32_t*>(dst + d) = *reinterpret_cast<const uint32_t*>(src + so);
+      }
+    return;
+  }
+  const int nv = J.cols * ESZ / 16;  // vectors per row
+  const int total = rows * nv;
+  for (int base = 0; base < total; base += NT * CU) {
+    u32x4_t v[CU];
+#pragma unroll
+    for (int u = 0; u < CU; ++u) {
+      const int i = base + threadIdx.x + u * NT;
+      if (i < total) {
+        const int r = i / nv, c = i - r * nv;
+        v[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(src + static_cast<int64_t>(r) * J.lds * ESZ) + c);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < CU; ++u) {
+      const int i = base + threadIdx.x + u * NT;
+      if (i < total) {
+        const int r = i / nv, c = i - r * nv;
+        __builtin_nontemporal_store(v[u], reinterpret_cast<u32x4_t*>(dst + static_cast<int64_t>(r) * J.ldd * ESZ) + c);
+      }
+    }
+  }
 }
 
 // Sum of one float per thread over the workgroup, in a fixed order (wave
@@ -278,6 +342,14 @@ hipError_t launch_rows_layernorm(const RowLaunch& L, const float* gamma, const f
 
 hipError_t launch_rows(const RowLaunch& L, hipStream_t s) {
   if (L.n_jobs <= 0 || L.max_rows <= 0 || L.n_chunks <= 0) return hipSuccess;
+  if (L.n_sum == 1 && L.tile_rows > 1 && L.n_chunks == 1) {
+    dim3 grid((L.max_rows + L.tile_rows - 1) / L.tile_rows, L.n_jobs);
+    if (L.elem_bytes == 2)
+      hipLaunchKernelGGL(rows_copy_tiled_kernel<2>, grid, dim3(NT), 0, s, L);
+    else
+      hipLaunchKernelGGL(rows_copy_tiled_kernel<4>, grid, dim3(NT), 0, s, L);
+    return hipGetLastError();
+  }
   dim3 grid(L.max_rows * L.n_chunks, L.n_jobs);
   if (L.elem_bytes == 2) {
     hipLaunchKernelGGL(rows_b16_copy_kernel, grid, dim3(NT), 0, s, L);
