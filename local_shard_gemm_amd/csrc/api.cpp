@@ -62,6 +62,16 @@ int32_t hip_fail(hipError_t e, const char* where) {
 // managed, or HIP-allocated / registered host memory. A plain host pointer
 // would fault the kernel, so it is refused here, after every other check
 // and before any launch.
+// The MFMA kernel reads B in 16-byte chunks; on a tile past column N the
+// chunk that holds column N-1 also covers up to 7 columns after it. Those
+// lie inside the row's leading dimension (ld is a multiple of 8), but on the
+// view's last row they must also lie inside the buffer, else the launch
+// takes the element-wise edge kernel (vec_ok = 0).
+bool b_rows_padded(const sm_buf* B, const BlockRef& rb) {
+  const i128 end = static_cast<i128>(rb.offset) + static_cast<i128>(rb.rows - 1) * B->ld + (rb.cols + 7) / 8 * 8;
+  return end <= B->elems;
+}
+
 int32_t check_device_memory(const void* ptr, const char* what) {
   hipPointerAttribute_t attr;
   const hipError_t e = hipPointerGetAttributes(&attr, ptr);
@@ -118,6 +128,7 @@ extern "C" int32_t sm_local_gemm(const sm_plan_t* plan, const sm_buf* A, const s
   };
   std::vector<Item> items;
   items.reserve(unit_count);
+  bool b_padded = true;
   const size_t csz = dtype_size(p.out_dtype);
   for (int32_t u = unit_begin; u < unit_begin + unit_count; ++u) {
     UnitView v;
@@ -145,6 +156,7 @@ extern "C" int32_t sm_local_gemm(const sm_plan_t* plan, const sm_buf* A, const s
     it.ptrs.a = static_cast<const uint16_t*>(A->ptr) + ra.off();
     it.ptrs.b = static_cast<const uint16_t*>(B->ptr) + rb.off();
     it.ptrs.c = static_cast<char*>(C->ptr) + rc.off() * static_cast<int64_t>(csz);
+    if (!b_rows_padded(B, rb)) b_padded = false;
     items.push_back(it);
   }
   if ((st = check_device_memory(A->ptr, "A")) || (st = check_device_memory(B->ptr, "B")) ||
@@ -176,6 +188,7 @@ extern "C" int32_t sm_local_gemm(const sm_plan_t* plan, const sm_buf* A, const s
     if (reinterpret_cast<uintptr_t>(it.ptrs.a) % 16 || reinterpret_cast<uintptr_t>(it.ptrs.b) % 16) L.vec_ok = 0;
     if (reinterpret_cast<uintptr_t>(it.ptrs.c) % 8) L.vec_c = 0;
   }
+  if (!b_padded) L.vec_ok = 0;
   const bool skinny = m <= kSkinnyMaxM;
   hipStream_t s = static_cast<hipStream_t>(stream);
   for (size_t first = 0; first < items.size(); first += kMaxUnitsPerLaunch) {
@@ -482,6 +495,7 @@ extern "C" int32_t sm_local_gemm_reduce(const sm_plan_t* plan, const sm_buf* A, 
     it.ptrs.a = static_cast<const uint16_t*>(A->ptr) + ra.off();
     it.ptrs.b = static_cast<const uint16_t*>(B->ptr) + rb.off();
     it.ptrs.c = static_cast<float*>(out->ptr) + coff;
+    if (!b_rows_padded(B, rb)) L.vec_ok = 0;
     if (reinterpret_cast<uintptr_t>(it.ptrs.a) % 16 || reinterpret_cast<uintptr_t>(it.ptrs.b) % 16) L.vec_ok = 0;
     if (reinterpret_cast<uintptr_t>(it.ptrs.c) % 8) L.vec_c = 0;
     items.push_back(it);

@@ -191,11 +191,15 @@ __device__ __forceinline__ void store_tile(const f32x16 (&acc)[4][4], void* C, c
 // fixed for the whole tile: each store is one instruction with a scalar base
 // and an immediate column offset, and the row arithmetic is scalar. Register
 // layouts as in store_tile.
-template <bool OUT_BF16, bool GELU>
+// GUARD: a ragged tile (past row M or column N of the view); only elements
+// inside the view are stored.
+template <bool OUT_BF16, bool GELU, bool GUARD>
 __device__ __forceinline__ void store_tile_interior(const f32x16 (&acc)[4][4], void* C, const GemmLaunch& L,
                                                     int row0, int col0, int wave) {
   const int lane = threadIdx.x & 63;
   const int wm = wave >> 1, wn = wave & 1;
+  // rows / columns of this wave's sub-tile still inside the view
+  const int rmax = GUARD ? L.M - row0 - wm * 128 : 128, cmax = GUARD ? L.N - col0 - wn * 128 : 128;
   const int64_t ldc = L.ldc;
   int64_t base;
   if (L.split_rows < L.M) {
@@ -213,11 +217,12 @@ __device__ __forceinline__ void store_tile_interior(const f32x16 (&acc)[4][4], v
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         float* rowp = cw + static_cast<int64_t>(mi * 32 + 8 * (v >> 2) + (v & 3)) * ldc;
+        const int rl = mi * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
 #pragma unroll
         for (int ni = 0; ni < 4; ++ni) {
           float x = acc[mi][ni][v];
           if (GELU) x = gelu_tanh_f32(x);
-          rowp[voff + ni * 32] = x;
+          if (!GUARD || (rl < rmax && ni * 32 + (lane & 31) < cmax)) rowp[voff + ni * 32] = x;
         }
       }
   } else {
@@ -226,10 +231,13 @@ __device__ __forceinline__ void store_tile_interior(const f32x16 (&acc)[4][4], v
 #pragma unroll
     for (int mi = 0; mi < 4; ++mi) {
       uint16_t* rowp = cw + static_cast<int64_t>(mi * 32) * ldc;
+      if (GUARD && mi * 32 + (lane & 31) >= rmax) continue;
 #pragma unroll
       for (int ni = 0; ni < 4; ++ni)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
+          const int cl = ni * 32 + 8 * g + 4 * (lane >> 5);  // first of this lane's 4 columns
+          if (GUARD && cl >= cmax) continue;
           float x[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
@@ -238,13 +246,14 @@ __device__ __forceinline__ void store_tile_interior(const f32x16 (&acc)[4][4], v
           }
           const uint32_t p01 = bf16x2_rne(x[0], x[1]), p23 = bf16x2_rne(x[2], x[3]);
           uint16_t* dst = rowp + voff + ni * 32 + 8 * g;
-          if (L.vec_c) {
+          if (L.vec_c && (!GUARD || cl + 3 < cmax)) {
             *reinterpret_cast<uint2*>(dst) = make_uint2(p01, p23);
           } else {
-            dst[0] = static_cast<uint16_t>(p01);
-            dst[1] = static_cast<uint16_t>(p01 >> 16);
-            dst[2] = static_cast<uint16_t>(p23);
-            dst[3] = static_cast<uint16_t>(p23 >> 16);
+            const uint16_t h[4] = {static_cast<uint16_t>(p01), static_cast<uint16_t>(p01 >> 16),
+                                   static_cast<uint16_t>(p23), static_cast<uint16_t>(p23 >> 16)};
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (!GUARD || cl + e < cmax) dst[e] = h[e];
           }
         }
     }
@@ -400,10 +409,24 @@ struct Frags {
   bf16x8 b[4];
 };
 
+// A wave-uniform pointer moved into scalar registers.
+__device__ __forceinline__ const char* uniform_ptr(const char* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v >> 32));
+  return reinterpret_cast<const char*>((static_cast<uint64_t>(hi) << 32) | lo);
+}
+
+// ragged: the tile runs past row M or column N of the view. Its lanes that
+// would load rows of A at or past M load row M-1 instead, and those that
+// would load columns of B at or past N load the chunk holding column N-1:
+// every load stays inside the views (no bounds on the loop's loads), and
+// the duplicated data only reaches outputs past row M or column N, which
+// are not stored.
 template <bool OUT_BF16, bool GELU>
 __device__ __forceinline__ void run_tile_lds(const GemmLaunch& L, const uint16_t* __restrict__ A,
                                              const uint16_t* __restrict__ B, void* C, int row0, int col0,
-                                             lds_char* smem) {
+                                             bool ragged, lds_char* smem) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
@@ -418,13 +441,18 @@ __device__ __forceinline__ void run_tile_lds(const GemmLaunch& L, const uint16_t
   for (int i = 0; i < 4; ++i) {
     const int ra = (4 * wave + i) * 16 + (lane >> 2);
     const int ca = (lane & 3) ^ ((ra >> 2) & 3);
-    va[i] = static_cast<int>((static_cast<int64_t>(ra) * lda + 8 * ca) * 2);
+    const int ra_src = ragged ? min(ra, L.M - 1 - row0) : ra;
+    va[i] = static_cast<int>((static_cast<int64_t>(ra_src) * lda + 8 * ca) * 2);
     const int rb = (4 * wave + i) * 2 + (lane >> 5);
     const int cb = (lane & 31) ^ ((rb & 3) << 2);
-    vb[i] = static_cast<int>((static_cast<int64_t>(rb) * ldb + 8 * cb) * 2);
+    const int cb_src = ragged ? min(8 * cb, ((L.N - 1) & ~7) - col0) : 8 * cb;
+    vb[i] = static_cast<int>((static_cast<int64_t>(rb) * ldb + cb_src) * 2);
   }
-  const char* a_tile = reinterpret_cast<const char*>(A + static_cast<int64_t>(row0) * lda);
-  const char* b_tile = reinterpret_cast<const char*>(B + col0);
+  // Tile bases in scalar registers: the buffer resources built from them
+  // each stage must be wave-uniform registers, and a base the compiler kept
+  // in vector registers would turn every load into a per-lane loop.
+  const char* a_tile = uniform_ptr(reinterpret_cast<const char*>(A + static_cast<int64_t>(row0) * lda));
+  const char* b_tile = uniform_ptr(reinterpret_cast<const char*>(B + col0));
   const int64_t a_step = BK2 * 2, b_step = static_cast<int64_t>(BK2) * ldb * 2;
 
   int a_off[2][4];
@@ -561,32 +589,37 @@ __device__ __forceinline__ void run_tile_lds(const GemmLaunch& L, const uint16_t
     if (kt + 2 < nk) iter(std::integral_constant<int, 1>{}, kt + 2, false);
   }
 
-  store_tile_interior<OUT_BF16, GELU>(acc, C, L, row0, col0, wave);
+  if (ragged)
+    store_tile_interior<OUT_BF16, GELU, true>(acc, C, L, row0, col0, wave);
+  else
+    store_tile_interior<OUT_BF16, GELU, false>(acc, C, L, row0, col0, wave);
 }
 
-// Interior tiles: every tile of the launch is a full BM x BN tile, K is a
-// multiple of 32 and every view is 16-byte aligned, so no load or store
-// needs a bounds check.
+// Every tile of every unit: full tiles, and ragged ones (the last tile row
+// past M, the last tile column past N), whose loads are clamped into the
+// views and whose stores are guarded. K is a multiple of 32 and every view
+// is 16-byte aligned (all_tiles_edge false).
 template <bool OUT_BF16, bool GELU>
 __global__ __launch_bounds__(NT, 1) void gemm_bf16_mfma_kernel(const GemmLaunch L) {
   __shared__ __attribute__((aligned(1024))) char smem[STAGES * STAGE_BYTES];
-  const int full_m = L.M / BM, full_n = L.N / BN;
-  const int VR = L.n_units * full_m;
-  const int T = VR * full_n;
+  const int VR = L.n_units * L.tiles_m;
+  const int T = VR * L.tiles_n;
   int vr, vc;
-  tile_of(blockIdx.x, T, VR, full_n, &vr, &vc);
-  const int unit = vr / full_m;
-  const int row0 = (vr - unit * full_m) * BM;
+  tile_of(blockIdx.x, T, VR, L.tiles_n, &vr, &vc);
+  const int unit = vr / L.tiles_m;
+  const int row0 = (vr - unit * L.tiles_m) * BM;
   const int col0 = vc * BN;
+  const bool ragged = row0 + BM > L.M || col0 + BN > L.N;
   const GemmUnitPtrs U = L.u[unit];
-  run_tile_lds<OUT_BF16, GELU>(L, U.a, U.b, U.c, row0, col0, (lds_char*)smem);
+  run_tile_lds<OUT_BF16, GELU>(L, U.a, U.b, U.c, row0, col0, ragged, (lds_char*)smem);
 }
 
-// Every tile goes to the edge kernel when K is not a multiple of 32, a view
+// The MFMA kernel takes every tile unless K is not a multiple of 32, a view
 // is not 16-byte aligned, a lane's byte offset inside a tile's buffer
 // resource (up to 255 rows of A, 31 rows of B) or a lane's element offset
 // inside an output tile (31 rows of C) would not fit in 31 bits, or a row
-// split of the output does not fall on tile boundaries.
+// split of the output does not fall on tile boundaries. Then every tile goes
+// to the edge kernel.
 __host__ __device__ __forceinline__ bool all_tiles_edge(const GemmLaunch& L) {
   constexpr int64_t kMaxOffset = int64_t{1} << 31;
   return (L.K % BK2) != 0 || !L.vec_ok || (static_cast<int64_t>(BM - 1) * L.lda + BK2) * 2 >= kMaxOffset ||
@@ -594,54 +627,28 @@ __host__ __device__ __forceinline__ bool all_tiles_edge(const GemmLaunch& L) {
          (L.split_rows < L.M && L.split_rows % BM != 0);
 }
 
-// Edge tiles: the last tile row (M % BM), the last tile column (N % BN), or
-// every tile (all_tiles_edge). Loads outside the views read as zero and
-// stores outside them are skipped. blockIdx.y = unit.
+// Edge kernel: every tile of the launch (all_tiles_edge). Loads outside the
+// views read as zero and stores outside them are skipped. blockIdx.y = unit.
 template <bool OUT_BF16, bool GELU>
 __global__ __launch_bounds__(NT, 1) void gemm_bf16_mfma_edge_kernel(const GemmLaunch L) {
   __shared__ uint4 lds[2 * 2 * BM * CH];
   const int unit = blockIdx.y;
-  int tm, tn;
-  if (all_tiles_edge(L)) {
-    tm = blockIdx.x / L.tiles_n;
-    tn = blockIdx.x % L.tiles_n;
-  } else {
-    const int e_rows = (L.M % BM) ? 1 : 0;
-    const int t = blockIdx.x;
-    if (t < e_rows * L.tiles_n) {
-      tm = L.tiles_m - 1;
-      tn = t;
-    } else {
-      tm = t - e_rows * L.tiles_n;
-      tn = L.tiles_n - 1;
-    }
-  }
+  const int tm = blockIdx.x / L.tiles_n;
+  const int tn = blockIdx.x % L.tiles_n;
   const GemmUnitPtrs U = L.u[unit];
   run_tile<true, OUT_BF16, GELU>(L, U.a, U.b, U.c, tm * BM, tn * BN, lds);
 }
 
 template <bool OUT_BF16, bool GELU>
 hipError_t launch_variant(const GemmLaunch& L, hipStream_t s) {
-  const int full_m = L.M / BM, full_n = L.N / BN;
-  const bool k_ragged = all_tiles_edge(L);
-  if (!k_ragged && full_m > 0 && full_n > 0) {
-    const int T = L.n_units * full_m * full_n;
+  if (!all_tiles_edge(L)) {
+    const int T = L.n_units * L.tiles_m * L.tiles_n;
     hipLaunchKernelGGL((gemm_bf16_mfma_kernel<OUT_BF16, GELU>), dim3(T), dim3(NT), 0, s, L);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
-  int n_edge;
-  if (k_ragged) {
-    n_edge = L.tiles_m * L.tiles_n;
   } else {
-    const int e_rows = (L.M % BM) ? 1 : 0, e_cols = (L.N % BN) ? 1 : 0;
-    n_edge = e_rows * L.tiles_n + e_cols * (L.tiles_m - e_rows);
+    hipLaunchKernelGGL((gemm_bf16_mfma_edge_kernel<OUT_BF16, GELU>), dim3(L.tiles_m * L.tiles_n, L.n_units), dim3(NT),
+                       0, s, L);
   }
-  if (n_edge > 0) {
-    hipLaunchKernelGGL((gemm_bf16_mfma_edge_kernel<OUT_BF16, GELU>), dim3(n_edge, L.n_units), dim3(NT), 0, s, L);
-    return hipGetLastError();
-  }
-  return hipSuccess;
+  return hipGetLastError();
 }
 
 }  // namespace

@@ -171,6 +171,33 @@ def test_store_paths_bitexact():
     assert guard_intact(fg, g.numel())
 
 
+def test_ragged_tiles_tight_buffers_bitexact():
+    """Ragged tiles read A rows and B columns clamped into the views. Two
+    layouts: (a) a B view whose last row ends exactly at the buffer's
+    declared end with N not a multiple of 8 (the 16-byte chunk holding column
+    N-1 would reach past it, so the launch goes to the element-wise kernel);
+    (b) the same product with the row padded (the MFMA pipeline kernel takes
+    the ragged tiles). Both bit for bit against the oracle, nothing outside C
+    written."""
+    say("case: ragged tiles, tight buffers")
+    I, J, K, ld = 300, 64, 70, 72
+    A, B = _int((I, J), 51), _int((J, K), 52)
+    p, q = _plans({"X": 1}, "P()", "P()", I, J, K)
+    Bp = torch.zeros(J, ld, dtype=torch.bfloat16)
+    Bp[:, :K] = B
+    Bd = to_dev(Bp)
+    want = ref.dense(A, B)
+    for elems in ((J - 1) * ld + K, J * ld):
+        bb = sm.sm_buf(Bd.data_ptr(), ld, 0, elems, sm.SM_BF16, 0)
+        fg, g = guarded((I, ld), torch.float32)
+        g.fill_(float("nan"))
+        sm.sm_local_gemm(p, sm.buf(to_dev(A)), bb, sm.buf(g))
+        gn = g.cpu().numpy()
+        assert f32_bits_equal(gn[:, :K], want), elems
+        assert np.isnan(gn[:, K:]).all()  # padding columns of C untouched
+        assert guard_intact(fg, g.numel())
+
+
 def test_gelu_epilogue_unaligned_views():
     """GeLU -> bfloat16 into the global H layout with column blocks of width 6:
     half of the views start off the 8-byte grid, so the bfloat16 stores go
