@@ -396,6 +396,8 @@ typedef __attribute__((address_space(3))) uint4 lds_u4;
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
 
 // s_waitcnt vmcnt(vm) lgkmcnt(lg) (expcnt unconstrained).
 template <int vm, int lg>
@@ -589,6 +591,62 @@ __device__ __forceinline__ void run_tile_lds(const GemmLaunch& L, const uint16_t
     if (kt + 2 < nk) iter(std::integral_constant<int, 1>{}, kt + 2, false);
   }
 
+  // K tail (K % 32 columns of A, rows of B): one more stage, loaded through
+  // registers with every element at or past K (and past the view's rows of
+  // A or columns of B) read as zero, and written into ring buffer 0 in the
+  // layout the buffer loads produce; then its two k16 steps.
+  const int k_tail = L.K - nk * BK2;
+  if (k_tail > 0) {
+    wait_cnt<0, 0>();
+    __builtin_amdgcn_s_barrier();  // every wave is done with the ring
+    asm volatile("" ::: "memory");
+    const int kb = nk * BK2;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int q = tid + NT * j;  // A: 256 rows x 4 chunks of 8 k
+      const int r = q >> 2, c = q & 3;
+      const int row = row0 + min(r, L.M - 1 - row0);
+      uint32_t w[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int k0 = kb + 8 * c + 2 * e;
+        const uint16_t* pa = A + static_cast<int64_t>(row) * lda + k0;
+        const uint32_t lo = k0 < L.K ? pa[0] : 0u, hi = k0 + 1 < L.K ? pa[1] : 0u;
+        w[e] = lo | (hi << 16);
+      }
+      *(lds_u32x4*)(smem + r * (BK2 * 2) + ((c ^ ((r >> 2) & 3)) << 4)) = u32x4{w[0], w[1], w[2], w[3]};
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int q = tid + NT * j;  // B: 32 rows (k) x 32 chunks of 8 columns
+      const int rb = q >> 5, cb = q & 31;
+      const int k = kb + rb;
+      uint32_t w[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int n0 = col0 + 8 * cb + 2 * e;
+        const uint16_t* pb = B + static_cast<int64_t>(k) * ldb + n0;
+        const uint32_t lo = (k < L.K && n0 < L.N) ? pb[0] : 0u, hi = (k < L.K && n0 + 1 < L.N) ? pb[1] : 0u;
+        w[e] = lo | (hi << 16);
+      }
+      *(lds_u32x4*)(smem + A_STAGE + rb * (BN * 2) + ((cb ^ ((rb & 3) << 2)) << 4)) = u32x4{w[0], w[1], w[2], w[3]};
+    }
+    wait_cnt<0, 0>();
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int i = 0; i < 12; ++i) read_item(F[0], 0, 0, i);
+#pragma unroll
+    for (int i = 0; i < 12; ++i) read_item(F[1], 0, 1, i);
+    wait_cnt<0, 0>();
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+      for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < 4; ++ni) acc[mi][ni] = mfma_block<OUT_BF16>(F[s2].a[mi], F[s2].b[ni], acc[mi][ni]);
+  }
+
   if (ragged)
     store_tile_interior<OUT_BF16, GELU, true>(acc, C, L, row0, col0, wave);
   else
@@ -597,8 +655,9 @@ __device__ __forceinline__ void run_tile_lds(const GemmLaunch& L, const uint16_t
 
 // Every tile of every unit: full tiles, and ragged ones (the last tile row
 // past M, the last tile column past N), whose loads are clamped into the
-// views and whose stores are guarded. K is a multiple of 32 and every view
-// is 16-byte aligned (all_tiles_edge false).
+// views and whose stores are guarded; a K that is not a multiple of 32 ends
+// with a zero-filled tail stage. Every view is 16-byte aligned
+// (all_tiles_edge false).
 template <bool OUT_BF16, bool GELU>
 __global__ __launch_bounds__(NT, 1) void gemm_bf16_mfma_kernel(const GemmLaunch L) {
   __shared__ __attribute__((aligned(1024))) char smem[STAGES * STAGE_BYTES];
@@ -614,15 +673,16 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16_mfma_kernel(const GemmLaunch 
   run_tile_lds<OUT_BF16, GELU>(L, U.a, U.b, U.c, row0, col0, ragged, (lds_char*)smem);
 }
 
-// The MFMA kernel takes every tile unless K is not a multiple of 32, a view
-// is not 16-byte aligned, a lane's byte offset inside a tile's buffer
+// The MFMA kernel takes every tile unless a view is not 16-byte aligned (or
+// the last row of a B view leaves no room for a 16-byte chunk past column
+// N, which the host folds into vec_ok), a lane's byte offset inside a tile's buffer
 // resource (up to 255 rows of A, 31 rows of B) or a lane's element offset
 // inside an output tile (31 rows of C) would not fit in 31 bits, or a row
 // split of the output does not fall on tile boundaries. Then every tile goes
 // to the edge kernel.
 __host__ __device__ __forceinline__ bool all_tiles_edge(const GemmLaunch& L) {
   constexpr int64_t kMaxOffset = int64_t{1} << 31;
-  return (L.K % BK2) != 0 || !L.vec_ok || (static_cast<int64_t>(BM - 1) * L.lda + BK2) * 2 >= kMaxOffset ||
+  return !L.vec_ok || (static_cast<int64_t>(BM - 1) * L.lda + BK2) * 2 >= kMaxOffset ||
          (static_cast<int64_t>(BK2 - 1) * L.ldb + BN) * 2 >= kMaxOffset || L.ldc * 32 >= kMaxOffset ||
          (L.split_rows < L.M && L.split_rows % BM != 0);
 }
