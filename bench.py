@@ -64,6 +64,21 @@ def setup(workload: str):
     return dict(w=w, A=A, B=B, p=p, Ad=Ad, Bd=Bd, P=P, out=out, mode=mode, I=I, J=J, K=K)
 
 
+def plan_time_us(ctx, reps: int = 2000) -> float:
+    """Host time of one sm_plan call on the workload's mesh and specs (the
+    binding's marshalling included), averaged over `reps` calls."""
+    import local_shard_gemm_amd as sm
+
+    w = ctx["w"]
+    names = [o.name for o in w.operands]
+    mesh, sa, sb = dict(w.mesh), w.operand(names[0]).spec, w.operand(names[1]).spec
+    sm.sm_plan(mesh, sa, sb, ctx["I"], ctx["J"], ctx["K"])
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        sm.sm_plan(mesh, sa, sb, ctx["I"], ctx["J"], ctx["K"])
+    return (time.perf_counter() - t0) / reps * 1e6
+
+
 def cpu_baseline(ctx, rows: int):
     """The oracle (fp64 naive loops) on a bounded sample of the same step:
     the first `rows` output rows of the local products, taken unit by unit
@@ -347,6 +362,20 @@ def main() -> int:
         t = once(reps)
         return once(10 * reps) if t < 0.2 else t
 
+    def single_launches(fn, reps):
+        """(median, min) ms of `reps` launches, each between its own two HIP
+        events on the kernels' stream (launches still queued back to back)."""
+        evs = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            evs.append((e0, e1))
+        torch.cuda.synchronize()
+        ts = sorted(e0.elapsed_time(e1) for e0, e1 in evs)
+        return ts[len(ts) // 2], ts[0]
+
     def cold(make_call, footprint: float):
         """Average launch duration without help from the 256 MB Infinity
         Cache, or None when one launch already moves 512 MiB or more (then
@@ -383,6 +412,8 @@ def main() -> int:
     # Per-kernel launch durations, each kernel on its own.
     gemm_avg = back_to_back(gemm, args.steps)
     red_avg = back_to_back(reduce, args.steps) if p.kase == sm.SM_CASE3 else 0.0
+    gemm_single = single_launches(gemm, args.steps)
+    plan_us = plan_time_us(ctx)
 
     m, n = p.c_local[0], p.c_local[1]
     kl = p.a_local[1]
@@ -475,7 +506,9 @@ def main() -> int:
                       + f" {p.n_groups} groups x {N} fp32 partials [{m},{n}]",
         },
         "ms_per_step_events": round(ms_step_events, 4),
+        "sm_plan_us": round(plan_us, 2),
         "gemm": {"avg_ms": round(gemm_avg, 4),
+                 "single_launch_median_ms": round(gemm_single[0], 4), "single_launch_min_ms": round(gemm_single[1], 4),
                  **({"cold_avg_ms": round(gemm_cold, 4),
                      "cold_gbps": round(gemm_bytes / (gemm_cold * 1e-3) / 1e9, 1)} if gemm_cold else {}),
                  "tflops": round(gemm_tflops, 1), "frac_of_peak": round(gemm_tflops / PEAK_BF16_TFLOPS, 4),
