@@ -207,7 +207,7 @@ int32_t sm_plan_gathered(const sm_plan_t* plan, sm_plan_t* out);
  *        stacked only (partials overlap in output coordinates, so a global
  *        layout is SM_ERR_UNREDUCED). Stacked output blocks are indexed
  *        relative to unit_begin.
- * Rows of at most 16 (a skinny batch) use a split-J streaming kernel; other
+ * Rows of at most 64 (a skinny batch) use a split-J streaming kernel; other
  * shapes use the LDS-tiled MFMA kernel. Errors: SM_ERR_NEEDS_GATHER for
  * case 2/4, SM_ERR_CASE for a GeLU epilogue on case 3. */
 int32_t sm_local_gemm(const sm_plan_t* plan, const sm_buf* A, const sm_buf* B,
@@ -244,7 +244,7 @@ int32_t sm_reduce_partials(const sm_plan_t* plan, const sm_buf* partials,
  *    coordinates), or stacked by (g - group_begin) * N + y ([m/N, n]).
  * A and B must use the global layout (block_stride 0). The result equals
  * sm_local_gemm + sm_reduce_partials up to fp32 summation order (bit for
- * bit on integer-valued inputs). Local products of at most 16 rows are
+ * bit on integer-valued inputs). Local products of at most 64 rows are
  * refused with SM_ERR_SHAPE (their split-J kernel needs the partials). */
 int32_t sm_local_gemm_reduce(const sm_plan_t* plan, const sm_buf* A, const sm_buf* B,
                              const sm_buf* out, int32_t mode, int32_t group_begin,

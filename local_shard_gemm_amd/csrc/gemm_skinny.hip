@@ -1,4 +1,4 @@
-// Split-J kernel for skinny local products (M <= 16 rows): each rank's
+// Split-J kernel for skinny local products (M <= 64 rows): each rank's
 // partial P_u = X_u . A_u with X_u [M, K] small and A_u [K, N] streamed
 // once from HBM. Used for the row-parallel step Z_i = X_i A_i with a small
 // batch (mbrenndoerfer.com "Row Parallelism": Z_i = X_i A_i; the partials
@@ -17,12 +17,15 @@
 //    registers, and issues 8 v_mfma_f32_32x32x16_bf16. Their B operand is
 //    exactly that layout (lane l: column l%32, k-group l/32): MFMA c covers
 //    the strided column set {n0 + 8j + c : j = 0..31}. X_u's fragment (row
-//    lane%32, 8 consecutive k) is a 16-byte load that stays in L2; rows
-//    M..31 of the MFMA are zero, so half of the matrix-core work is padding
-//    on a path that keeps the matrix cores under 10 % busy.
+//    lane%32, 8 consecutive k) is a 16-byte load that stays in L2.
+//  * Rows come in blocks of 32 (the MFMA's rows): RB = 1 block for M <= 32,
+//    2 for M <= 64, 8 MFMAs per block and step. Rows past M read as zero.
+//    At M = 16 half of the matrix-core work is padding; at M = 64 the
+//    matrix cores are still far from limiting (16 MFMAs per 8 KiB of A per
+//    wave), so the kernel stays bound by HBM.
 //  * The next step's 8 loads are in flight while a step's MFMAs run.
 //  * The 4 wave partials are added in LDS in wave order (a fixed order, so
-//    the result is deterministic) and stored once.
+//    the result is deterministic), 32 rows per pass, and stored once.
 #include "device_math.h"
 #include "kernels.h"
 
@@ -36,7 +39,8 @@ constexpr int WAVES = 4;
 constexpr int NT = 64 * WAVES;
 constexpr int COLS = 256;  // output columns per workgroup
 constexpr int KSTEP = 16;  // rows of A per MFMA step
-constexpr int MROWS = 16;  // output rows kept (M <= 16)
+// Output rows per reduction pass: one MFMA row block (32), or 16 when M <=
+// 16, which halves the reduction buffer (64 KiB: two workgroups fit a CU).
 
 __device__ __forceinline__ uint4 load16(const uint16_t* p) {
   return *reinterpret_cast<const uint4*>(p);
@@ -78,20 +82,25 @@ __device__ __forceinline__ void transpose8(const uint4 (&in)[8], uint4 (&out)[8]
 }
 
 
+template <int RB>
 struct StepRegs {
-  uint4 x;      // X fragment
+  uint4 x[RB];  // X fragments, one per 32-row block
   uint4 a[8];   // 8 rows x 8 columns of A
 };
 
-template <bool EDGE>
-__device__ __forceinline__ void load_step(StepRegs& r, const uint16_t* X, int64_t ldx, const uint16_t* A,
+template <bool EDGE, int RB>
+__device__ __forceinline__ void load_step(StepRegs<RB>& r, const uint16_t* X, int64_t ldx, const uint16_t* A,
                                           int64_t lda, int M, int K, int N, int k0, int n0, int h, int j,
                                           bool vec) {
   const int kx = k0 + 8 * h;
-  if (EDGE || j >= M)
-    r.x = load16_guarded(X, ldx, j, kx, M, K, vec);
-  else
-    r.x = load16(X + static_cast<int64_t>(j) * ldx + kx);
+#pragma unroll
+  for (int b = 0; b < RB; ++b) {
+    const int row = 32 * b + j;
+    if (EDGE || row >= M)
+      r.x[b] = load16_guarded(X, ldx, row, kx, M, K, vec);
+    else
+      r.x[b] = load16(X + static_cast<int64_t>(row) * ldx + kx);
+  }
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     if (EDGE)
@@ -101,9 +110,9 @@ __device__ __forceinline__ void load_step(StepRegs& r, const uint16_t* X, int64_
   }
 }
 
-template <bool EDGE, bool OUT_BF16, bool GELU>
+template <bool EDGE, bool OUT_BF16, bool GELU, int RB, int PROWS>
 __global__ __launch_bounds__(NT) void gemm_skinny_kernel(const GemmLaunch L) {
-  __shared__ float red[WAVES][MROWS][COLS];
+  __shared__ float red[WAVES][PROWS][COLS];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int h = lane >> 5, j = lane & 31;
   const int n0 = blockIdx.x * COLS;
@@ -115,61 +124,81 @@ __global__ __launch_bounds__(NT) void gemm_skinny_kernel(const GemmLaunch L) {
   const int s_begin = (steps * wave) / WAVES;
   const int s_end = (steps * (wave + 1)) / WAVES;
 
-  f32x16 acc[8];
+  f32x16 acc[RB][8];
 #pragma unroll
-  for (int c = 0; c < 8; ++c)
+  for (int b = 0; b < RB; ++b)
 #pragma unroll
-    for (int v = 0; v < 16; ++v) acc[c][v] = 0.f;
+    for (int c = 0; c < 8; ++c)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[b][c][v] = 0.f;
 
   // One set of load registers: once a step's block has been transposed into
   // the MFMA operands, the load registers take the next step's loads while
-  // the 8 MFMAs run.
-  StepRegs r;
+  // the MFMAs run.
+  StepRegs<RB> r;
   if (s_begin < s_end) load_step<EDGE>(r, U.a, L.lda, U.b, L.ldb, M, K, N, s_begin * KSTEP, n0, h, j, L.vec_ok);
   for (int s = s_begin; s < s_end; ++s) {
     uint4 t[8];
     transpose8(r.a, t);
-    const bf16x8 xf = __builtin_bit_cast(bf16x8, r.x);
+    bf16x8 xf[RB];
+#pragma unroll
+    for (int b = 0; b < RB; ++b) xf[b] = __builtin_bit_cast(bf16x8, r.x[b]);
     if (s + 1 < s_end) load_step<EDGE>(r, U.a, L.lda, U.b, L.ldb, M, K, N, (s + 1) * KSTEP, n0, h, j, L.vec_ok);
 #pragma unroll
-    for (int c = 0; c < 8; ++c)
-      acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xf, __builtin_bit_cast(bf16x8, t[c]), acc[c], 0, 0, 0);
+    for (int b = 0; b < RB; ++b)
+#pragma unroll
+      for (int c = 0; c < 8; ++c)
+        acc[b][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xf[b], __builtin_bit_cast(bf16x8, t[c]), acc[b][c], 0, 0, 0);
   }
 
-  // Output of MFMA c, register v: row 8(v/4) + 4h + v%4, column n0 + 8j + c.
-  // Registers 0..7 hold rows 0..15; registers 8..15 hold the zero rows.
+  // Output of MFMA (b, c), register v: row 32b + 8(v/4) + 4h + v%4, column
+  // n0 + 8j + c. One reduction pass per row block, rows past M skipped.
 #pragma unroll
-  for (int c = 0; c < 8; ++c)
+  for (int b = 0; b < RB; ++b) {
+    const int rows = min(PROWS, M - 32 * b);
+    if (b > 0) __syncthreads();  // the previous pass has read red
 #pragma unroll
-    for (int v = 0; v < 8; ++v) red[wave][8 * (v >> 2) + 4 * h + (v & 3)][8 * j + c] = acc[c][v];
-  __syncthreads();
-
-  for (int o = tid; o < MROWS * COLS; o += NT) {
-    const int m = o / COLS, col = o % COLS;
-    float sum = red[0][m][col];
+    for (int c = 0; c < 8; ++c)
 #pragma unroll
-    for (int w = 1; w < WAVES; ++w) sum += red[w][m][col];
-    const int n = n0 + col;
-    if (m < M && n < N) {
-      if (GELU) sum = gelu_tanh_f32(sum);
-      const int64_t off = static_cast<int64_t>(m) * L.ldc + n;
-      if (OUT_BF16)
-        static_cast<uint16_t*>(U.c)[off] = bf16_rne(sum);
-      else
-        static_cast<float*>(U.c)[off] = sum;
+      for (int v = 0; v < 16; ++v) {
+        const int m = 8 * (v >> 2) + 4 * h + (v & 3);
+        if (m < rows) red[wave][m][8 * j + c] = acc[b][c][v];
+      }
+    __syncthreads();
+    for (int o = tid; o < rows * COLS; o += NT) {
+      const int m = o / COLS, col = o % COLS;
+      float sum = red[0][m][col];
+#pragma unroll
+      for (int w = 1; w < WAVES; ++w) sum += red[w][m][col];
+      const int n = n0 + col;
+      if (n < N) {
+        if (GELU) sum = gelu_tanh_f32(sum);
+        const int64_t off = static_cast<int64_t>(32 * b + m) * L.ldc + n;
+        if (OUT_BF16)
+          static_cast<uint16_t*>(U.c)[off] = bf16_rne(sum);
+        else
+          static_cast<float*>(U.c)[off] = sum;
+      }
     }
   }
 }
 
-template <bool OUT_BF16, bool GELU>
-hipError_t launch_variant(const GemmLaunch& L, hipStream_t s) {
+template <bool OUT_BF16, bool GELU, int RB, int PROWS>
+hipError_t launch_rb(const GemmLaunch& L, hipStream_t s) {
   const bool edge = (L.N % COLS) != 0 || (L.K % KSTEP) != 0 || !L.vec_ok;
   dim3 grid((L.N + COLS - 1) / COLS, L.n_units);
   if (edge)
-    hipLaunchKernelGGL((gemm_skinny_kernel<true, OUT_BF16, GELU>), grid, dim3(NT), 0, s, L);
+    hipLaunchKernelGGL((gemm_skinny_kernel<true, OUT_BF16, GELU, RB, PROWS>), grid, dim3(NT), 0, s, L);
   else
-    hipLaunchKernelGGL((gemm_skinny_kernel<false, OUT_BF16, GELU>), grid, dim3(NT), 0, s, L);
+    hipLaunchKernelGGL((gemm_skinny_kernel<false, OUT_BF16, GELU, RB, PROWS>), grid, dim3(NT), 0, s, L);
   return hipGetLastError();
+}
+
+template <bool OUT_BF16, bool GELU>
+hipError_t launch_variant(const GemmLaunch& L, hipStream_t s) {
+  if (L.M <= 16) return launch_rb<OUT_BF16, GELU, 1, 16>(L, s);
+  if (L.M <= 32) return launch_rb<OUT_BF16, GELU, 1, 32>(L, s);
+  return launch_rb<OUT_BF16, GELU, 2, 32>(L, s);
 }
 
 }  // namespace

@@ -76,6 +76,6 @@ constexpr int kLayerNormMaxCols = 32768;
 // Tile sizes of the MFMA kernel (host side uses them for the grid).
 constexpr int kTileM = 256, kTileN = 256, kTileK = 64;
 // Rows handled by the skinny split-J kernel.
-constexpr int kSkinnyMaxM = 16;
+constexpr int kSkinnyMaxM = 64;
 
 }  // namespace shardmm

@@ -278,19 +278,20 @@ def test_gathered_plan_examples():
 
 
 def test_fused_reduce_validation():
-    p3 = sm.sm_plan({"X": 2}, "P(None, 'X')", "P('X', None)", 64, 128, 64)
+    p3 = sm.sm_plan({"X": 2}, "P(None, 'X')", "P('X', None)", 160, 128, 64)
     p1 = sm.sm_plan({"X": 2}, "P('X', None)", "P()", 64, 128, 64)
     p2 = sm.sm_plan({"X": 2}, "P(None, 'X')", "P()", 64, 128, 64)
-    sk = sm.sm_plan({"X": 2}, "P(None, 'X')", "P('X', None)", 16, 128, 64)
     A, B, out = _fb(128, dt=BF), _fb(64, dt=BF), _fb(64)
     assert _err(sm.sm_local_gemm_reduce, p1, A, B, out) == sm.SM_ERR_CASE
     assert _err(sm.sm_local_gemm_reduce, p2, A, B, out) == sm.SM_ERR_NEEDS_GATHER
     assert _err(sm.sm_local_gemm_reduce, p3, _fb(128, 64 * 128, dt=BF), B, out) == sm.SM_ERR_ARG
-    assert _err(sm.sm_local_gemm_reduce, sk, A, B, out) == sm.SM_ERR_SHAPE
+    for rows in (16, 64):  # skinny products (at most 64 rows) reduce through sm_reduce_partials
+        sk = sm.sm_plan({"X": 2}, "P(None, 'X')", "P('X', None)", rows, 128, 64)
+        assert _err(sm.sm_local_gemm_reduce, sk, A, B, out) == sm.SM_ERR_SHAPE
     assert _err(sm.sm_local_gemm_reduce, p3, A, B, out, 9) == sm.SM_ERR_ARG
     assert _err(sm.sm_local_gemm_reduce, p3, A, B, _fb(64, 16 * 64, elems=2 * 16 * 64), sm.SM_REDUCESCATTER) \
         == sm.SM_ERR_SHAPE
-    q = sm.sm_plan({"X": 3}, "P(None, 'X')", "P('X', None)", 64, 96, 64)
+    q = sm.sm_plan({"X": 3}, "P(None, 'X')", "P('X', None)", 160, 96, 64)
     assert _err(sm.sm_local_gemm_reduce, q, _fb(96, dt=BF), B, out, sm.SM_REDUCESCATTER) == sm.SM_ERR_INDIVISIBLE
 
 

@@ -287,6 +287,11 @@ SKINNY = [
     ({"X": 2}, "P()", "P(None, 'X')", 16, 96, 2 * 128),              # case 1, skinny
     ({"T": 2}, "P(None, 'T')", "P('T', None)", 16, 2 * 112, 768),   # 7 K steps over 4 waves, 3 column blocks
     ({"T": 2}, "P(None, 'T')", "P('T', None)", 3, 2 * 16, 512),     # one K step: three waves idle
+    ({"T": 4}, "P(None, 'T')", "P('T', None)", 17, 4 * 128, 512),   # one row block, rows 16..31 kept
+    ({"T": 4}, "P(None, 'T')", "P('T', None)", 32, 4 * 96, 264),    # one full row block, ragged N
+    ({"T": 2}, "P(None, 'T')", "P('T', None)", 33, 2 * 128, 256),   # two row blocks, second has one row
+    ({"T": 8}, "P(None, 'T')", "P('T', None)", 64, 8 * 256, 1024),  # two full row blocks
+    ({"T": 4}, "P(None, 'T')", "P('T', None)", 48, 4 * 100, 296),   # two row blocks, ragged K and N
 ]
 
 
@@ -305,19 +310,20 @@ def test_skinny_shapes_bitexact(case):
     assert guard_intact(full, P.numel())
 
 
+@pytest.mark.parametrize("rows", [12, 40], ids=["rows12", "rows40"])
 @pytest.mark.parametrize("width", [256, 288], ids=["interior", "ragged"])
-def test_gelu_epilogue_skinny(width):
-    """The GeLU(tanh) -> bfloat16 epilogue on the skinny path (M <= 16):
+def test_gelu_epilogue_skinny(width, rows):
+    """The GeLU(tanh) -> bfloat16 epilogue on the skinny path (M <= 64):
     column blocks of a small batch, within the derived bound of the oracle's
     round_bf16(gelu(.))."""
-    say("case: gelu epilogue skinny", width)
+    say("case: gelu epilogue skinny", width, rows)
     F = 4 * width
-    X = wl.random_normal((12, 160), 34)
+    X = wl.random_normal((rows, 160), 34)
     W1 = wl.random_normal((160, F), 35, 0.1)
     W2 = wl.random_normal((F, 64), 36, 0.1)
-    p1, q1 = _plans({"T": 4}, "P(None, None)", "P(None, 'T')", 12, 160, F, sm.SM_BF16)
-    _, q2 = _plans({"T": 4}, "P(None, 'T')", "P('T', None)", 12, F, 64)
-    H = torch.empty(12, F, dtype=torch.bfloat16, device=DEV)
+    p1, q1 = _plans({"T": 4}, "P(None, None)", "P(None, 'T')", rows, 160, F, sm.SM_BF16)
+    _, q2 = _plans({"T": 4}, "P(None, 'T')", "P('T', None)", rows, F, 64)
+    H = torch.empty(rows, F, dtype=torch.bfloat16, device=DEV)
     sm.sm_local_gemm(p1, sm.buf(to_dev(X)), sm.buf(to_dev(W1)), sm.buf(H), sm.SM_EPI_GELU_TANH)
     Hw, _ = ref.mlp_chain(q1, q2, X, W1, W2)
     Hg = H.cpu().view(torch.int16).numpy().view(np.uint16)
@@ -572,7 +578,7 @@ def test_host_memory_refused_before_launch():
     refused on the host with SM_ERR_ARG before anything is launched; the
     device outputs are untouched."""
     say("case: host memory refused")
-    I, J, K = 64, 128, 64
+    I, J, K = 128, 128, 64  # more than 64 rows: not a skinny product, so the fused call gets as far as the buffers
     A, B = _int((I, J), 71), _int((J, K), 72)
     p, q = _plans({"X": 2}, "P(None, 'X')", "P('X', None)", I, J, K)
     Ad, Bd = to_dev(A), to_dev(B)
