@@ -419,6 +419,55 @@ __device__ __forceinline__ const char* uniform_ptr(const char* p) {
   return reinterpret_cast<const char*>((static_cast<uint64_t>(hi) << 32) | lo);
 }
 
+// bfloat16 epilogue of a full interior tile through LDS (the ring is free
+// once the K loop is done): every wave writes its 128x128 sub-tile (after
+// GeLU, rounded) into a row-major 256x256 bfloat16 image (128 KiB; 16-byte
+// chunk c of row r at c ^ (r & 31), which spreads both the 8-byte writes of
+// 32 consecutive rows and the 16-byte reads of one row over the banks), then
+// the workgroup stores whole rows: each store instruction writes two rows of
+// 512 contiguous bytes. Stored straight from the MFMA layout, each
+// instruction wrote 16 bytes to each of 32 rows, and the partial lines
+// doubled the HBM write traffic (WRITE_SIZE twice the bytes of H).
+template <bool GELU>
+__device__ __forceinline__ void store_tile_bf16_staged(const f32x16 (&acc)[4][4], uint16_t* ct, int64_t ldc, int wave,
+                                                       lds_char* smem) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wm = wave >> 1, wn = wave & 1;
+  wait_cnt<0, 0>();
+  __builtin_amdgcn_s_barrier();  // every wave is done with the ring
+  asm volatile("" ::: "memory");
+#pragma unroll
+  for (int mi = 0; mi < 4; ++mi) {
+    const int r = wm * 128 + mi * 32 + (lane & 31);
+#pragma unroll
+    for (int ni = 0; ni < 4; ++ni)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int c = wn * 128 + ni * 32 + 8 * g + 4 * (lane >> 5);
+        float x[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          x[e] = acc[mi][ni][4 * g + e];
+          if (GELU) x[e] = gelu_tanh_f32(x[e]);
+        }
+        typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+        typedef __attribute__((address_space(3))) u32x2 lds_u32x2;
+        *(lds_u32x2*)(smem + r * 512 + ((((c >> 3) ^ (r & 31))) << 4) + ((c >> 2) & 1) * 8) =
+            u32x2{bf16x2_rne(x[0], x[1]), bf16x2_rne(x[2], x[3])};
+      }
+  }
+  wait_cnt<0, 0>();
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+#pragma unroll 4
+  for (int it = 0; it < 32; ++it) {
+    const int q = tid + NT * it;
+    const int r = q >> 5, ch = q & 31;
+    const u32x4 v = *(lds_u32x4*)(smem + r * 512 + ((ch ^ (r & 31)) << 4));
+    *reinterpret_cast<u32x4*>(ct + static_cast<int64_t>(r) * ldc + ch * 8) = v;
+  }
+}
+
 // ragged: the tile runs past row M or column N of the view. Its lanes that
 // would load rows of A at or past M load row M-1 instead, and those that
 // would load columns of B at or past N load the chunk holding column N-1:
@@ -647,10 +696,26 @@ __device__ __forceinline__ void run_tile_lds(const GemmLaunch& L, const uint16_t
         for (int ni = 0; ni < 4; ++ni) acc[mi][ni] = mfma_block<OUT_BF16>(F[s2].a[mi], F[s2].b[ni], acc[mi][ni]);
   }
 
-  if (ragged)
+  if (ragged) {
     store_tile_interior<OUT_BF16, GELU, true>(acc, C, L, row0, col0, wave);
-  else
+  } else if constexpr (OUT_BF16) {
+    // whole rows through LDS when the tile's rows start on 16 bytes (the
+    // view's start; ldc is a multiple of 8 and col0 of 256)
+    int64_t base;
+    if (L.split_rows < L.M) {
+      const int blk = row0 / L.split_rows;
+      base = blk * L.split_stride + static_cast<int64_t>(row0 - blk * L.split_rows) * L.ldc;
+    } else {
+      base = static_cast<int64_t>(row0) * L.ldc;
+    }
+    uint16_t* ct = static_cast<uint16_t*>(C) + base + col0;
+    if ((reinterpret_cast<uintptr_t>(ct) & 15) == 0)
+      store_tile_bf16_staged<GELU>(acc, ct, L.ldc, wave, smem);
+    else
+      store_tile_interior<OUT_BF16, GELU, false>(acc, C, L, row0, col0, wave);
+  } else {
     store_tile_interior<OUT_BF16, GELU, false>(acc, C, L, row0, col0, wave);
+  }
 }
 
 // Every tile of every unit: full tiles, and ragged ones (the last tile row
