@@ -186,7 +186,7 @@ extern "C" int32_t sm_local_gemm(const sm_plan_t* plan, const sm_buf* A, const s
   L.vec_c = 1;
   for (const Item& it : items) {
     if (reinterpret_cast<uintptr_t>(it.ptrs.a) % 16 || reinterpret_cast<uintptr_t>(it.ptrs.b) % 16) L.vec_ok = 0;
-    if (reinterpret_cast<uintptr_t>(it.ptrs.c) % 8) L.vec_c = 0;
+    if (reinterpret_cast<uintptr_t>(it.ptrs.c) % (L.out_bf16 ? 8 : 16)) L.vec_c = 0;
   }
   if (!b_padded) L.vec_ok = 0;
   const bool skinny = m <= kSkinnyMaxM;
@@ -497,7 +497,7 @@ extern "C" int32_t sm_local_gemm_reduce(const sm_plan_t* plan, const sm_buf* A, 
     it.ptrs.c = static_cast<float*>(out->ptr) + coff;
     if (!b_rows_padded(B, rb)) L.vec_ok = 0;
     if (reinterpret_cast<uintptr_t>(it.ptrs.a) % 16 || reinterpret_cast<uintptr_t>(it.ptrs.b) % 16) L.vec_ok = 0;
-    if (reinterpret_cast<uintptr_t>(it.ptrs.c) % 8) L.vec_c = 0;
+    if (reinterpret_cast<uintptr_t>(it.ptrs.c) % 16) L.vec_c = 0;  // float32 partial sums
     items.push_back(it);
   }
   if ((st = check_device_memory(A->ptr, "A")) || (st = check_device_memory(B->ptr, "B")) ||

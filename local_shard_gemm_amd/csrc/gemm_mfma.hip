@@ -5,13 +5,14 @@
 // sharding sandbox "Local matmul"; lingze.zone "Case 1" and "Case 3").
 //
 // Two kernels share the 256x256 output tile per workgroup of 4 waves (2x2),
-// each wave owning a 128x128 sub-tile = 4x4 MFMA blocks of
-// v_mfma_f32_32x32x16_bf16 (256 fp32 accumulators per lane):
-//  * gemm_bf16_mfma_kernel (interior tiles): direct HBM -> LDS buffer loads,
-//    transposing LDS reads, a 5-stage LDS ring and three register fragment
+// each wave owning a 128x128 sub-tile (256 fp32 accumulators per lane):
+//  * gemm_bf16_mfma_kernel (every tile when the views are 16-byte aligned):
+//    8x8 blocks of v_mfma_f32_16x16x32_bf16, direct HBM -> LDS buffer loads,
+//    transposing LDS reads, a 5-stage LDS ring and two register fragment
 //    sets; described above run_tile_lds.
-//  * gemm_bf16_mfma_edge_kernel (ragged M/N/K, unaligned views): guarded
-//    loads through registers, described here.
+//  * gemm_bf16_mfma_edge_kernel (unaligned views): 4x4 blocks of
+//    v_mfma_f32_32x32x16_bf16, guarded loads through registers, described
+//    here.
 //
 // Edge-tile design:
 //  * K advances 64 at a time through two LDS buffers (2 x 64 KiB): the
@@ -185,81 +186,6 @@ __device__ __forceinline__ void store_tile(const f32x16 (&acc)[4][4], void* C, c
   }
 }
 
-// Epilogue of an interior tile. The tile lies inside one output block (the
-// host sends launches whose row split would cut a tile to the edge kernel),
-// so every store address is a wave-uniform row base plus a per-lane offset
-// fixed for the whole tile: each store is one instruction with a scalar base
-// and an immediate column offset, and the row arithmetic is scalar. Register
-// layouts as in store_tile.
-// GUARD: a ragged tile (past row M or column N of the view); only elements
-// inside the view are stored.
-template <bool OUT_BF16, bool GELU, bool GUARD>
-__device__ __forceinline__ void store_tile_interior(const f32x16 (&acc)[4][4], void* C, const GemmLaunch& L,
-                                                    int row0, int col0, int wave) {
-  const int lane = threadIdx.x & 63;
-  const int wm = wave >> 1, wn = wave & 1;
-  // rows / columns of this wave's sub-tile still inside the view
-  const int rmax = GUARD ? L.M - row0 - wm * 128 : 128, cmax = GUARD ? L.N - col0 - wn * 128 : 128;
-  const int64_t ldc = L.ldc;
-  int64_t base;
-  if (L.split_rows < L.M) {
-    const int blk = row0 / L.split_rows;
-    base = blk * L.split_stride + static_cast<int64_t>(row0 - blk * L.split_rows) * ldc;
-  } else {
-    base = static_cast<int64_t>(row0) * ldc;
-  }
-  base += static_cast<int64_t>(wm * 128) * ldc + col0 + wn * 128;
-  if constexpr (!OUT_BF16) {
-    float* cw = static_cast<float*>(C) + base;
-    const int voff = (lane >> 5) * 4 * static_cast<int>(ldc) + (lane & 31);
-#pragma unroll
-    for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        float* rowp = cw + static_cast<int64_t>(mi * 32 + 8 * (v >> 2) + (v & 3)) * ldc;
-        const int rl = mi * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-#pragma unroll
-        for (int ni = 0; ni < 4; ++ni) {
-          float x = acc[mi][ni][v];
-          if (GELU) x = gelu_tanh_f32(x);
-          if (!GUARD || (rl < rmax && ni * 32 + (lane & 31) < cmax)) rowp[voff + ni * 32] = x;
-        }
-      }
-  } else {
-    uint16_t* cw = static_cast<uint16_t*>(C) + base;
-    const int voff = (lane & 31) * static_cast<int>(ldc) + 4 * (lane >> 5);
-#pragma unroll
-    for (int mi = 0; mi < 4; ++mi) {
-      uint16_t* rowp = cw + static_cast<int64_t>(mi * 32) * ldc;
-      if (GUARD && mi * 32 + (lane & 31) >= rmax) continue;
-#pragma unroll
-      for (int ni = 0; ni < 4; ++ni)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int cl = ni * 32 + 8 * g + 4 * (lane >> 5);  // first of this lane's 4 columns
-          if (GUARD && cl >= cmax) continue;
-          float x[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            x[e] = acc[mi][ni][4 * g + e];
-            if (GELU) x[e] = gelu_tanh_f32(x[e]);
-          }
-          const uint32_t p01 = bf16x2_rne(x[0], x[1]), p23 = bf16x2_rne(x[2], x[3]);
-          uint16_t* dst = rowp + voff + ni * 32 + 8 * g;
-          if (L.vec_c && (!GUARD || cl + 3 < cmax)) {
-            *reinterpret_cast<uint2*>(dst) = make_uint2(p01, p23);
-          } else {
-            const uint16_t h[4] = {static_cast<uint16_t>(p01), static_cast<uint16_t>(p01 >> 16),
-                                   static_cast<uint16_t>(p23), static_cast<uint16_t>(p23 >> 16)};
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-              if (!GUARD || cl + e < cmax) dst[e] = h[e];
-          }
-        }
-    }
-  }
-}
-
 template <bool EDGE, bool OUT_BF16, bool GELU>
 __device__ __forceinline__ void run_tile(const GemmLaunch& L, const uint16_t* __restrict__ A,
                                          const uint16_t* __restrict__ B, void* C, int row0, int col0,
@@ -357,7 +283,7 @@ __device__ __forceinline__ void run_tile(const GemmLaunch& L, const uint16_t* __
 }
 
 // ---------------------------------------------------------------------------
-// Interior tiles: direct HBM -> LDS pipeline.
+// Interior tiles: direct HBM -> LDS pipeline, v_mfma_f32_16x16x32_bf16.
 //
 //  * Both operands travel global -> LDS with buffer_load_dwordx4 ... lds (16
 //    bytes per lane, landing at M0 + 16 * lane): no staging registers, no
@@ -365,24 +291,46 @@ __device__ __forceinline__ void run_tile(const GemmLaunch& L, const uint16_t* __
 //    tile is fixed; the k advance moves the buffer resource's base (scalar
 //    arithmetic), so a load costs no vector instructions.
 //  * K advances 32 at a time through a ring of 5 LDS stages of 32 KiB (A
-//    256x32, B 32x256; 160 KiB, the whole LDS); loads run 3 stages ahead of
-//    the stage being read.
+//    256x32, B 32x256; 160 KiB, the whole LDS); loads run 4 stages ahead of
+//    the stage whose MFMAs run (a stage's buffer is refilled as soon as its
+//    fragments are in registers).
+//  * Each wave's 128x128 sub-tile is 8x8 blocks of 16x16; one stage is one
+//    k32 step of 64 MFMAs on 8 A and 8 B fragments. The 16x16x32 shape moves
+//    half the accumulator data per flop of the 32x32x16 one, and under the
+//    board's power limit on random data it holds a higher clock for the
+//    same work.
+//  * Blocks accumulate C^T (the B fragment goes in the first operand): lane
+//    l holds C[16 mi + l%16][16 ni + 4(l/16) + e], e < 4, four consecutive
+//    columns of one row.
 //  * A stage: row r holds 32 k (64 bytes = 4 chunks); chunk c of row r sits
-//    at c ^ ((r >> 2) & 3). A fragments are 16-byte LDS reads (8 k of one
-//    row per lane).
+//    at c ^ a_swz(r), a_swz(r) = (row bit 2) << 1. An A fragment is one
+//    16-byte LDS read per lane (8 k of row l%16, chunk l/16).
+//  * Choosing the swizzle: a 16-byte LDS read serves 16 lanes a cycle, and
+//    the conflict counters show the 16 are not 16 consecutive lanes: the
+//    former swizzle (r >> 2) & 3 and a bit-swapped one both read at half
+//    rate here, while the 32x32 layout's pattern and a contiguous 1 KiB
+//    read run at the 4-cycle minimum. Modelling the lanes served together
+//    as the cosets of a 4-dimensional XOR subspace of lane-index bits, 32
+//    subspaces fit those four measurements. A row-major layout maps lane
+//    bits to the 16 slots of a 256-byte window linearly, with a 2-dimensional
+//    kernel, and reads without conflicts iff that kernel meets none of the
+//    32; a_swz's kernel (lanes 0, 8, 36, 44) is one that does. A fragment
+//    order (block-contiguous 1 KiB reads) also avoids the conflicts, but
+//    its DMA touches 16 rows per 16 lanes and starved the pipeline.
 //  * B stage: row k holds 256 n (512 bytes = 32 chunks); chunk c of row k
-//    sits at c ^ ((k & 3) << 2). B stays N-contiguous in LDS; the MFMA's
-//    k-packed fragment is read with ds_read_b64_tr_b16, which (per 16-lane
-//    group) takes lane 4r+q's 4 consecutive elements as row r, columns
-//    4q..4q+3 of a 4x16 tile and returns column j to lane j. Two such reads
-//    give a lane the 8 k values of its column.
-//  * Both swizzles make every fragment read touch each LDS bank the minimum
-//    number of times.
-//  * Three fragment sets: the fragments of k16 step t+2 are read while the
-//    MFMAs of step t run, so an LDS read has two steps (32 MFMAs) to land
-//    instead of one. With two sets the waves spent about a quarter of their
-//    time waiting on fragment reads that the stage's DMA traffic had
-//    delayed.
+//    sits at c ^ b_swz(k), b_swz(k) = ((k & 3) << 2) | (((k >> 3) & 1) << 1).
+//    B stays N-contiguous in LDS; the MFMA's k-packed fragment is read with
+//    ds_read_b64_tr_b16, which (per 16-lane group) takes lane 4r+q's 4
+//    consecutive elements as row r, columns 4q..4q+3 of a 4x16 tile and
+//    returns column j to lane j. Two such reads give a lane the 8 k values
+//    of its column. The (k & 3) term spreads the 4 rows of one group over
+//    the banks; the k-bit-3 term moves the group reading k 8..15 to the
+//    other 32-byte halves, so the two groups served together fill a
+//    256-byte window (without it they collide, also at half rate).
+//  * Two fragment sets: stage kt+1's 24 fragment reads ride on every other
+//    MFMA of the first 48 of stage kt, which leaves each read at least 17
+//    MFMAs to land; the fragment registers a read overwrites were last used
+//    at least 15 MFMAs earlier.
 // ---------------------------------------------------------------------------
 constexpr int BK2 = 32;
 constexpr int STAGES = 5;
@@ -395,9 +343,55 @@ typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) uint4 lds_u4;
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
-typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) u32x2 lds_u32x2;
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ int b_swz(int k) { return ((k & 3) << 2) | (((k >> 3) & 1) << 1); }
+// A chunk swizzle: chunk bit 1 flips with row bit 2.
+__device__ __forceinline__ int a_swz(int r) { return ((r >> 2) & 1) << 1; }
+// bfloat16 epilogue image: chunk swizzle of row r (16-byte chunks, 32 a row).
+__device__ __forceinline__ int e_swz(int r) { return (r ^ ((r & 1) << 2)) & 31; }
+
+// One 16x16 block, accumulating C^T in place. Written as an instruction so
+// that the accumulator stays in one AGPR quad (the "+a" tie) and the
+// fragments in VGPRs: the compiler's own MFMA form for this shape splits the
+// 256 accumulators between both files and copies them around every MFMA.
+// The compiler sees no MFMA here, so the hazards it would pad are covered
+// by construction:
+//  * every accumulator is written once per 64 MFMAs;
+//  * fragment registers are rewritten only by LDS reads issued at least 15
+//    MFMAs after their last use, and each stage starts by waiting for every
+//    LDS read (lgkmcnt 0);
+//  * acc_fence() after the zero fill keeps that fill ahead of the prologue's
+//    loads, far from the first MFMA;
+//  * acc_drain() pads 24 wait states after the last MFMA and then claims
+//    every accumulator, so no compiler-placed read of one (a spill, a store)
+//    can come before the padding.
+__device__ __forceinline__ void mfma16(const bf16x8& a, const bf16x8& b, f32x4& c) {
+  asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(b), "v"(a));
+}
+__device__ __forceinline__ void acc_fence(f32x4 (&acc)[8][8]) {
+#pragma unroll
+  for (int mi = 0; mi < 8; ++mi)
+    asm volatile("" : "+a"(acc[mi][0]), "+a"(acc[mi][1]), "+a"(acc[mi][2]), "+a"(acc[mi][3]), "+a"(acc[mi][4]),
+                 "+a"(acc[mi][5]), "+a"(acc[mi][6]), "+a"(acc[mi][7]));
+}
+// 24 wait states >= the 8-pass MFMA's write-to-read distance.
+__device__ __forceinline__ void acc_drain(f32x4 (&acc)[8][8]) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+  acc_fence(acc);
+}
+// One block's accumulators moved to VGPRs where the epilogue uses them:
+// left to itself the compiler copied all 256 out of the AGPRs at once after
+// the K loop and spilled.
+__device__ __forceinline__ f32x4 acc_take(const f32x4& a) {
+  f32x4 v;
+  asm volatile("" : "=v"(v) : "0"(a));
+  return v;
+}
 
 // s_waitcnt vmcnt(vm) lgkmcnt(lg) (expcnt unconstrained).
 template <int vm, int lg>
@@ -407,8 +401,8 @@ __device__ __forceinline__ void wait_cnt() {
 }
 
 struct Frags {
-  bf16x8 a[4];
-  bf16x8 b[4];
+  bf16x8 a[8];
+  bf16x8 b[8];
 };
 
 // A wave-uniform pointer moved into scalar registers.
@@ -419,17 +413,90 @@ __device__ __forceinline__ const char* uniform_ptr(const char* p) {
   return reinterpret_cast<const char*>((static_cast<uint64_t>(hi) << 32) | lo);
 }
 
+// Element offset of the tile's first row in C (its output block when the
+// rows are split).
+__device__ __forceinline__ int64_t tile_row_base(const GemmLaunch& L, int row0) {
+  if (L.split_rows < L.M) {
+    const int blk = row0 / L.split_rows;
+    return blk * L.split_stride + static_cast<int64_t>(row0 - blk * L.split_rows) * L.ldc;
+  }
+  return static_cast<int64_t>(row0) * L.ldc;
+}
+
+// Epilogue of an interior tile straight from the registers. The tile lies
+// inside one output block (the host sends launches whose row split would cut
+// a tile to the edge kernel), so every store address is a wave-uniform row
+// base plus a per-lane offset fixed for the whole tile. Per block a lane
+// stores its 4 consecutive columns: one 16-byte (float32) or 8-byte
+// (bfloat16) store when the C views start on 4 elements (L.vec_c), else
+// element by element.
+// GUARD: a ragged tile (past row M or column N of the view); only elements
+// inside the view are stored.
+template <bool OUT_BF16, bool GELU, bool GUARD>
+__device__ __forceinline__ void store_tile_interior(const f32x4 (&acc)[8][8], void* C, const GemmLaunch& L,
+                                                    int row0, int col0, int wave) {
+  const int lane = threadIdx.x & 63;
+  const int wm = wave >> 1, wn = wave & 1;
+  // rows / columns of this wave's sub-tile still inside the view
+  const int rmax = GUARD ? L.M - row0 - wm * 128 : 128, cmax = GUARD ? L.N - col0 - wn * 128 : 128;
+  const int64_t ldc = L.ldc;
+  const int64_t base = tile_row_base(L, row0) + static_cast<int64_t>(wm * 128) * ldc + col0 + wn * 128;
+  const int lr = lane & 15, lc = 4 * (lane >> 4);
+  const int voff = lr * static_cast<int>(ldc) + lc;
+  const bool vec = L.vec_c != 0;
+#pragma unroll
+  for (int mi = 0; mi < 8; ++mi) {
+    if (GUARD && mi * 16 + lr >= rmax) continue;
+#pragma unroll
+    for (int ni = 0; ni < 8; ++ni) {
+      const int cl = ni * 16 + lc;  // first of this lane's 4 columns
+      if (GUARD && cl >= cmax) continue;
+      const f32x4 v = acc_take(acc[mi][ni]);
+      float x[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        x[e] = v[e];
+        if (GELU) x[e] = gelu_tanh_f32(x[e]);
+      }
+      const bool whole = vec && (!GUARD || cl + 3 < cmax);
+      if constexpr (!OUT_BF16) {
+        float* dst = static_cast<float*>(C) + base + static_cast<int64_t>(mi * 16) * ldc + voff + ni * 16;
+        if (whole) {
+          *reinterpret_cast<f32x4*>(dst) = f32x4{x[0], x[1], x[2], x[3]};
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (!GUARD || cl + e < cmax) dst[e] = x[e];
+        }
+      } else {
+        uint16_t* dst = static_cast<uint16_t*>(C) + base + static_cast<int64_t>(mi * 16) * ldc + voff + ni * 16;
+        const uint32_t p01 = bf16x2_rne(x[0], x[1]), p23 = bf16x2_rne(x[2], x[3]);
+        if (whole) {
+          *reinterpret_cast<uint2*>(dst) = make_uint2(p01, p23);
+        } else {
+          const uint16_t h[4] = {static_cast<uint16_t>(p01), static_cast<uint16_t>(p01 >> 16),
+                                 static_cast<uint16_t>(p23), static_cast<uint16_t>(p23 >> 16)};
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (!GUARD || cl + e < cmax) dst[e] = h[e];
+        }
+      }
+    }
+  }
+}
+
 // bfloat16 epilogue of a full interior tile through LDS (the ring is free
 // once the K loop is done): every wave writes its 128x128 sub-tile (after
 // GeLU, rounded) into a row-major 256x256 bfloat16 image (128 KiB; 16-byte
-// chunk c of row r at c ^ (r & 31), which spreads both the 8-byte writes of
-// 32 consecutive rows and the 16-byte reads of one row over the banks), then
+// chunk c of row r at c ^ e_swz(r): 16 consecutive rows take distinct
+// chunks for the 8-byte writes, and rows 2i, 2i+1, read in the same cycles,
+// differ in chunk bit 2 for the 16-byte reads), then
 // the workgroup stores whole rows: each store instruction writes two rows of
-// 512 contiguous bytes. Stored straight from the MFMA layout, each
-// instruction wrote 16 bytes to each of 32 rows, and the partial lines
-// doubled the HBM write traffic (WRITE_SIZE twice the bytes of H).
+// 512 contiguous bytes. Stored straight from the registers, each instruction
+// writes 32 bytes to each of 16 rows, and such partial lines doubled the HBM
+// write traffic.
 template <bool GELU>
-__device__ __forceinline__ void store_tile_bf16_staged(const f32x16 (&acc)[4][4], uint16_t* ct, int64_t ldc, int wave,
+__device__ __forceinline__ void store_tile_bf16_staged(const f32x4 (&acc)[8][8], uint16_t* ct, int64_t ldc, int wave,
                                                        lds_char* smem) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wm = wave >> 1, wn = wave & 1;
@@ -437,24 +504,21 @@ __device__ __forceinline__ void store_tile_bf16_staged(const f32x16 (&acc)[4][4]
   __builtin_amdgcn_s_barrier();  // every wave is done with the ring
   asm volatile("" ::: "memory");
 #pragma unroll
-  for (int mi = 0; mi < 4; ++mi) {
-    const int r = wm * 128 + mi * 32 + (lane & 31);
+  for (int mi = 0; mi < 8; ++mi) {
+    const int r = wm * 128 + mi * 16 + (lane & 15);
 #pragma unroll
-    for (int ni = 0; ni < 4; ++ni)
+    for (int ni = 0; ni < 8; ++ni) {
+      const int c = wn * 128 + ni * 16 + 4 * (lane >> 4);
+      const f32x4 v = acc_take(acc[mi][ni]);
+      float x[4];
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int c = wn * 128 + ni * 32 + 8 * g + 4 * (lane >> 5);
-        float x[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          x[e] = acc[mi][ni][4 * g + e];
-          if (GELU) x[e] = gelu_tanh_f32(x[e]);
-        }
-        typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-        typedef __attribute__((address_space(3))) u32x2 lds_u32x2;
-        *(lds_u32x2*)(smem + r * 512 + ((((c >> 3) ^ (r & 31))) << 4) + ((c >> 2) & 1) * 8) =
-            u32x2{bf16x2_rne(x[0], x[1]), bf16x2_rne(x[2], x[3])};
+      for (int e = 0; e < 4; ++e) {
+        x[e] = v[e];
+        if (GELU) x[e] = gelu_tanh_f32(x[e]);
       }
+      *(lds_u32x2*)(smem + r * 512 + (((c >> 3) ^ e_swz(r)) << 4) + ((c >> 2) & 1) * 8) =
+          u32x2{bf16x2_rne(x[0], x[1]), bf16x2_rne(x[2], x[3])};
+    }
   }
   wait_cnt<0, 0>();
   __builtin_amdgcn_s_barrier();
@@ -463,7 +527,7 @@ __device__ __forceinline__ void store_tile_bf16_staged(const f32x16 (&acc)[4][4]
   for (int it = 0; it < 32; ++it) {
     const int q = tid + NT * it;
     const int r = q >> 5, ch = q & 31;
-    const u32x4 v = *(lds_u32x4*)(smem + r * 512 + ((ch ^ (r & 31)) << 4));
+    const u32x4 v = *(lds_u32x4*)(smem + r * 512 + ((ch ^ e_swz(r)) << 4));
     *reinterpret_cast<u32x4*>(ct + static_cast<int64_t>(r) * ldc + ch * 8) = v;
   }
 }
@@ -491,11 +555,11 @@ __device__ __forceinline__ void run_tile_lds(const GemmLaunch& L, const uint16_t
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int ra = (4 * wave + i) * 16 + (lane >> 2);
-    const int ca = (lane & 3) ^ ((ra >> 2) & 3);
+    const int ca = (lane & 3) ^ a_swz(ra);
     const int ra_src = ragged ? min(ra, L.M - 1 - row0) : ra;
     va[i] = static_cast<int>((static_cast<int64_t>(ra_src) * lda + 8 * ca) * 2);
     const int rb = (4 * wave + i) * 2 + (lane >> 5);
-    const int cb = (lane & 31) ^ ((rb & 3) << 2);
+    const int cb = (lane & 31) ^ b_swz(rb);
     const int cb_src = ragged ? min(8 * cb, ((L.N - 1) & ~7) - col0) : 8 * cb;
     vb[i] = static_cast<int>((static_cast<int64_t>(rb) * ldb + cb_src) * 2);
   }
@@ -506,34 +570,33 @@ __device__ __forceinline__ void run_tile_lds(const GemmLaunch& L, const uint16_t
   const char* b_tile = uniform_ptr(reinterpret_cast<const char*>(B + col0));
   const int64_t a_step = BK2 * 2, b_step = static_cast<int64_t>(BK2) * ldb * 2;
 
-  int a_off[2][4];
-  int b_off[2][4][2];
+  // ---- fragment offsets inside a stage buffer.
+  // A block mi: row wm*128 + 16 mi + l%16, chunk l/16. The swizzle reads
+  // row bit 2, which comes from the lane alone, so block mi sits 1 KiB
+  // after block 0.
+  const int ar = wm * 128 + (lane & 15);
+  const int a_off = ar * (BK2 * 2) + (((lane >> 4) ^ a_swz(ar)) << 4);
+  // B block ni: columns wn*128 + 16 ni + 4q (q = l%4) of rows 8g + rr
+  // (g = l/16, rr = (l/4)%4) for the first read and 4 rows further for the
+  // second; both rows have the same swizzle, so the second read sits 2 KiB
+  // after the first.
+  int b_off[8];
+  {
+    const int kr = 8 * (lane >> 4) + ((lane >> 2) & 3);
 #pragma unroll
-  for (int s = 0; s < 2; ++s) {
-#pragma unroll
-    for (int mi = 0; mi < 4; ++mi) {
-      const int r = wm * 128 + mi * 32 + (lane & 31);
-      const int c = 2 * s + (lane >> 5);
-      a_off[s][mi] = r * (BK2 * 2) + ((c ^ ((r >> 2) & 3)) << 4);
+    for (int ni = 0; ni < 8; ++ni) {
+      const int col = wn * 128 + ni * 16 + 4 * (lane & 3);
+      b_off[ni] = A_STAGE + kr * (BN * 2) + (((col >> 3) ^ b_swz(kr)) << 4) + ((col >> 2) & 1) * 8;
     }
-    const int g = lane >> 4, j = lane & 15, rr = j >> 2, q = j & 3, h = lane >> 5;
-#pragma unroll
-    for (int ni = 0; ni < 4; ++ni)
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const int kr = 16 * s + 8 * h + 4 * t + rr;
-        const int col = wn * 128 + ni * 32 + 16 * (g & 1) + 4 * q;
-        const int ch = col >> 3, half = (col >> 2) & 1;
-        b_off[s][ni][t] = A_STAGE + kr * (BN * 2) + ((ch ^ ((kr & 3) << 2)) << 4) + half * 8;
-      }
   }
-  auto read_item = [&](Frags& F, int sb, int s, int item) {
+  // Item i < 8: A fragment i; item 8 + 2 ni + t: read t of B fragment ni.
+  auto read_item = [&](Frags& F, int sb, int item) __attribute__((always_inline)) {
     lds_char* st = smem + sb;
-    if (item < 4) {
-      F.a[item] = __builtin_bit_cast(bf16x8, *(lds_u4*)(st + a_off[s][item]));
+    if (item < 8) {
+      F.a[item] = __builtin_bit_cast(bf16x8, *(lds_u4*)(st + a_off + item * 1024));
     } else {
-      const int ni = (item - 4) >> 1, t = (item - 4) & 1;
-      const bf16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(st + b_off[s][ni][t]));
+      const int ni = (item - 8) >> 1, t = (item - 8) & 1;
+      const bf16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(st + b_off[ni] + t * 2048));
       if (t == 0)
         F.b[ni] = __builtin_shufflevector(v, F.b[ni].hi, 0, 1, 2, 3, 4, 5, 6, 7);
       else
@@ -541,7 +604,7 @@ __device__ __forceinline__ void run_tile_lds(const GemmLaunch& L, const uint16_t
     }
   };
   // DMA item of stage kt_load into the stage buffer at byte offset sb.
-  auto dma_item = [&](int kt_load, int sb, int item) {
+  auto dma_item = [&](int kt_load, int sb, int item) __attribute__((always_inline)) {
     if (item < 4) {
       const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
           (void*)(a_tile + kt_load * a_step), (short)0, 0x7fffffff, 0x00020000);
@@ -554,96 +617,101 @@ __device__ __forceinline__ void run_tile_lds(const GemmLaunch& L, const uint16_t
     }
   };
 
-  f32x16 acc[4][4];
+  f32x4 acc[8][8];
 #pragma unroll
-  for (int mi = 0; mi < 4; ++mi)
+  for (int mi = 0; mi < 8; ++mi)
 #pragma unroll
-    for (int ni = 0; ni < 4; ++ni)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[mi][ni][v] = 0.0f;
+    for (int ni = 0; ni < 8; ++ni) acc[mi][ni] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  acc_fence(acc);
 
-  // One k16 step: 16 MFMAs on `cur`; the 12 fragment reads of the step two
-  // ahead ride one per MFMA on the first 12 (if rd), DMA items
-  // [dma0, dma0 + 4) on MFMAs 3, 7, 11, 15 (if ld).
-  auto step = [&](const Frags& cur, Frags& nxt, bool rd, int sb_rd, int s_rd, bool ld, int kt_load, int sb_ld,
-                  int dma0) {
+  // One stage: 64 MFMAs on `cur`; the 24 fragment reads of the next stage
+  // ride on every other MFMA from 0 to 46 (if rd), the 8 DMA items of stage
+  // kt_load on MFMAs 8j+5 (if ld). Spread this way the stage ran 6 % faster
+  // than with the reads on MFMAs 0..23 and the DMA after them; bunching the
+  // DMA early in the stage was 5-12 % slower.
+  // The lambdas are forced inline: inlined later, the LDS reads lost the
+  // alias information that tells the compiler they do not touch the
+  // in-flight LDS loads, and it waited for every load (vmcnt 0) before
+  // them.
+  auto stage = [&](const Frags& cur, Frags& nxt, bool rd, int sb_rd, bool ld, int kt_load, int sb_ld) __attribute__((always_inline)) {
 #pragma unroll
-    for (int idx = 0; idx < 16; ++idx) {
-      const int mi = idx >> 2, ni = idx & 3;
-      acc[mi][ni] = mfma_block<OUT_BF16>(cur.a[mi], cur.b[ni], acc[mi][ni]);
-      if (idx < 12 && rd) read_item(nxt, sb_rd, s_rd, idx);
-      if ((idx & 3) == 3 && ld) dma_item(kt_load, sb_ld, dma0 + (idx >> 2));
+    for (int idx = 0; idx < 64; ++idx) {
+      const int mi = idx >> 3, ni = idx & 7;
+      mfma16(cur.a[mi], cur.b[ni], acc[mi][ni]);
+      if (idx < 48 && (idx & 1) == 0 && rd) read_item(nxt, sb_rd, idx >> 1);
+      if ((idx & 7) == 5 && ld) dma_item(kt_load, sb_ld, idx >> 3);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
 
   const int nk = L.K / BK2;
   constexpr int RING = STAGES * STAGE_BYTES;
-  Frags F[3];
-  // prologue: stages 0..3 in flight, then stage 0's fragments
+  Frags F[2];
+  // prologue: stages 0..4 in flight, then stage 0's fragments
 #pragma unroll
-  for (int p = 0; p < STAGES - 1; ++p)
+  for (int p = 0; p < STAGES; ++p)
     if (p < nk) {
 #pragma unroll
       for (int it = 0; it < 8; ++it) dma_item(p, p * STAGE_BYTES, it);
     }
-  if (nk > 3) wait_cnt<24, 15>();
+  if (nk > 4) wait_cnt<32, 15>();
+  else if (nk == 4) wait_cnt<24, 15>();
   else if (nk == 3) wait_cnt<16, 15>();
   else if (nk == 2) wait_cnt<8, 15>();
   else wait_cnt<0, 15>();
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
+  if (nk > 0) {
 #pragma unroll
-  for (int i = 0; i < 12; ++i) read_item(F[0], 0, 0, i);
-#pragma unroll
-  for (int i = 0; i < 12; ++i) read_item(F[1], 0, 1, i);
+    for (int i = 0; i < 24; ++i) read_item(F[0], 0, i);
+  }
 
-  int sb_rd = STAGE_BYTES;                    // buffer of stage kt+1
-  int sb_ld = (STAGES - 1) * STAGE_BYTES;     // buffer of stage kt+4
-  // Iteration kt: steps 2kt and 2kt+1 on F[(2kt)%3], F[(2kt+1)%3]; stage
-  // kt+1's fragments into the other two sets; stage kt+4 into the buffer
-  // stage kt-1 used.
-  auto iter = [&](auto phase_c, int kt, bool steady) {
-    constexpr int P = decltype(phase_c)::value;  // (2kt) % 3
-    constexpr int P0 = P, P1 = (P + 1) % 3, P2 = (P + 2) % 3;
+  int sb_cur = 0;             // buffer of stage kt
+  int sb_rd = STAGE_BYTES;    // buffer of stage kt+1
+  // Iteration kt: the MFMAs of stage kt on F[kt % 2]; stage kt+1's
+  // fragments into the other set; stage kt+5 into stage kt's buffer. That
+  // buffer is free: its fragments were read in iteration kt-1, and every
+  // wave waited for its reads (lgkmcnt 0) before this iteration's barrier.
+  // Loads run 4 stages ahead.
+  auto iter = [&](auto parity_c, int kt, bool steady) __attribute__((always_inline)) {
+    constexpr int P = decltype(parity_c)::value;  // kt % 2
     const bool rd = steady || kt + 1 < nk;
-    const bool ld = steady || kt + STAGES - 1 < nk;
+    const bool ld = steady || kt + STAGES < nk;
     __builtin_amdgcn_sched_barrier(0);
-    if (steady || kt + STAGES - 2 < nk)
-      wait_cnt<16, 12>();
+    // stage kt+1 landed; stages kt+2 .. kt+4 may still be in flight
+    if (steady || kt + 4 < nk)
+      wait_cnt<24, 0>();
+    else if (kt + 3 < nk)
+      wait_cnt<16, 0>();
+    else if (kt + 2 < nk)
+      wait_cnt<8, 0>();
     else
-      wait_cnt<0, 12>();
+      wait_cnt<0, 0>();
     asm volatile("" ::: "memory");
     if (rd) __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
-    step(F[P0], F[P2], rd, sb_rd, 0, ld, kt + STAGES - 1, sb_ld, 0);
-    if (rd)
-      wait_cnt<63, 12>();
-    else
-      wait_cnt<63, 0>();
-    __builtin_amdgcn_sched_barrier(0);
-    step(F[P1], F[P0], rd, sb_rd, 1, ld, kt + STAGES - 1, sb_ld, 4);
+    stage(F[P], F[P ^ 1], rd, sb_rd, ld, kt + STAGES, sb_cur);
+    sb_cur = sb_rd;
     sb_rd = sb_rd + STAGE_BYTES == RING ? 0 : sb_rd + STAGE_BYTES;
-    sb_ld = sb_ld + STAGE_BYTES == RING ? 0 : sb_ld + STAGE_BYTES;
   };
 
   int kt = 0;
-  for (; kt + 2 + STAGES - 1 < nk; kt += 3) {
+  for (; kt + 1 + STAGES < nk; kt += 2) {
     iter(std::integral_constant<int, 0>{}, kt, true);
-    iter(std::integral_constant<int, 2>{}, kt + 1, true);
-    iter(std::integral_constant<int, 1>{}, kt + 2, true);
+    iter(std::integral_constant<int, 1>{}, kt + 1, true);
   }
-  for (; kt < nk; kt += 3) {
+  for (; kt < nk; kt += 2) {
     iter(std::integral_constant<int, 0>{}, kt, false);
-    if (kt + 1 < nk) iter(std::integral_constant<int, 2>{}, kt + 1, false);
-    if (kt + 2 < nk) iter(std::integral_constant<int, 1>{}, kt + 2, false);
+    if (kt + 1 < nk) iter(std::integral_constant<int, 1>{}, kt + 1, false);
   }
+
+  acc_drain(acc);
 
   // K tail (K % 32 columns of A, rows of B): one more stage, loaded through
   // registers with every element at or past K (and past the view's rows of
   // A or columns of B) read as zero, and written into ring buffer 0 in the
-  // layout the buffer loads produce; then its two k16 steps.
+  // layout the buffer loads produce; then its 64 MFMAs.
   const int k_tail = L.K - nk * BK2;
   if (k_tail > 0) {
     wait_cnt<0, 0>();
@@ -663,7 +731,7 @@ __device__ __forceinline__ void run_tile_lds(const GemmLaunch& L, const uint16_t
         const uint32_t lo = k0 < L.K ? pa[0] : 0u, hi = k0 + 1 < L.K ? pa[1] : 0u;
         w[e] = lo | (hi << 16);
       }
-      *(lds_u32x4*)(smem + r * (BK2 * 2) + ((c ^ ((r >> 2) & 3)) << 4)) = u32x4{w[0], w[1], w[2], w[3]};
+      *(lds_u32x4*)(smem + r * (BK2 * 2) + ((c ^ a_swz(r)) << 4)) = u32x4{w[0], w[1], w[2], w[3]};
     }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -678,22 +746,19 @@ __device__ __forceinline__ void run_tile_lds(const GemmLaunch& L, const uint16_t
         const uint32_t lo = (k < L.K && n0 < L.N) ? pb[0] : 0u, hi = (k < L.K && n0 + 1 < L.N) ? pb[1] : 0u;
         w[e] = lo | (hi << 16);
       }
-      *(lds_u32x4*)(smem + A_STAGE + rb * (BN * 2) + ((cb ^ ((rb & 3) << 2)) << 4)) = u32x4{w[0], w[1], w[2], w[3]};
+      *(lds_u32x4*)(smem + A_STAGE + rb * (BN * 2) + ((cb ^ b_swz(rb)) << 4)) = u32x4{w[0], w[1], w[2], w[3]};
     }
     wait_cnt<0, 0>();
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
 #pragma unroll
-    for (int i = 0; i < 12; ++i) read_item(F[0], 0, 0, i);
-#pragma unroll
-    for (int i = 0; i < 12; ++i) read_item(F[1], 0, 1, i);
+    for (int i = 0; i < 24; ++i) read_item(F[0], 0, i);
     wait_cnt<0, 0>();
 #pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2)
+    for (int mi = 0; mi < 8; ++mi)
 #pragma unroll
-      for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-        for (int ni = 0; ni < 4; ++ni) acc[mi][ni] = mfma_block<OUT_BF16>(F[s2].a[mi], F[s2].b[ni], acc[mi][ni]);
+      for (int ni = 0; ni < 8; ++ni) mfma16(F[0].a[mi], F[0].b[ni], acc[mi][ni]);
+    acc_drain(acc);
   }
 
   if (ragged) {
@@ -701,14 +766,7 @@ __device__ __forceinline__ void run_tile_lds(const GemmLaunch& L, const uint16_t
   } else if constexpr (OUT_BF16) {
     // whole rows through LDS when the tile's rows start on 16 bytes (the
     // view's start; ldc is a multiple of 8 and col0 of 256)
-    int64_t base;
-    if (L.split_rows < L.M) {
-      const int blk = row0 / L.split_rows;
-      base = blk * L.split_stride + static_cast<int64_t>(row0 - blk * L.split_rows) * L.ldc;
-    } else {
-      base = static_cast<int64_t>(row0) * L.ldc;
-    }
-    uint16_t* ct = static_cast<uint16_t*>(C) + base + col0;
+    uint16_t* ct = static_cast<uint16_t*>(C) + tile_row_base(L, row0) + col0;
     if ((reinterpret_cast<uintptr_t>(ct) & 15) == 0)
       store_tile_bf16_staged<GELU>(acc, ct, L.ldc, wave, smem);
     else

@@ -29,7 +29,7 @@ struct GemmLaunch {
   int32_t epilogue;          // kEpiStore / kEpiGelu
   int32_t out_bf16;          // 1: store bfloat16 (RNE), 0: float32
   int32_t vec_ok;            // 1: every A/B view starts 16-byte aligned
-  int32_t vec_c;             // 1: every C view starts 8-byte aligned (bf16 vector stores)
+  int32_t vec_c;             // 1: every C view starts on 4 elements (8 bytes bf16, 16 float32): vector stores
   // Output rows in blocks: row r goes to c + (r / split_rows) * split_stride
   // + (r % split_rows) * ldc (split_rows >= M: one plain [M, N] block).
   int32_t split_rows;
