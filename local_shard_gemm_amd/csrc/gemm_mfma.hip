@@ -37,6 +37,7 @@
 //    so their tiles stack into one tall virtual matrix.
 #include "device_math.h"
 #include "kernels.h"
+#include "mfma16.h"
 
 #include <type_traits>
 
@@ -347,7 +348,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) u32x2 lds_u32x2;
-typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef mfma_f32x4 f32x4;
 
 __device__ __forceinline__ int b_swz(int k) { return ((k & 3) << 2) | (((k >> 3) & 1) << 1); }
 // A chunk swizzle: chunk bit 1 flips with row bit 2.
@@ -355,43 +356,16 @@ __device__ __forceinline__ int a_swz(int r) { return ((r >> 2) & 1) << 1; }
 // bfloat16 epilogue image: chunk swizzle of row r (16-byte chunks, 32 a row).
 __device__ __forceinline__ int e_swz(int r) { return (r ^ ((r & 1) << 2)) & 31; }
 
-// One 16x16 block, accumulating C^T in place. Written as an instruction so
-// that the accumulator stays in one AGPR quad (the "+a" tie) and the
-// fragments in VGPRs: the compiler's own MFMA form for this shape splits the
-// 256 accumulators between both files and copies them around every MFMA.
-// The compiler sees no MFMA here, so the hazards it would pad are covered
-// by construction:
+// One 16x16 block, accumulating C^T in place (the B fragment is the first
+// operand); the instruction and its hazard rules are in mfma16.h. Here:
 //  * every accumulator is written once per 64 MFMAs;
 //  * fragment registers are rewritten only by LDS reads issued at least 15
 //    MFMAs after their last use, and each stage starts by waiting for every
 //    LDS read (lgkmcnt 0);
-//  * acc_fence() after the zero fill keeps that fill ahead of the prologue's
-//    loads, far from the first MFMA;
-//  * acc_drain() pads 24 wait states after the last MFMA and then claims
-//    every accumulator, so no compiler-placed read of one (a spill, a store)
-//    can come before the padding.
-__device__ __forceinline__ void mfma16(const bf16x8& a, const bf16x8& b, f32x4& c) {
-  asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(b), "v"(a));
-}
-__device__ __forceinline__ void acc_fence(f32x4 (&acc)[8][8]) {
-#pragma unroll
-  for (int mi = 0; mi < 8; ++mi)
-    asm volatile("" : "+a"(acc[mi][0]), "+a"(acc[mi][1]), "+a"(acc[mi][2]), "+a"(acc[mi][3]), "+a"(acc[mi][4]),
-                 "+a"(acc[mi][5]), "+a"(acc[mi][6]), "+a"(acc[mi][7]));
-}
-// 24 wait states >= the 8-pass MFMA's write-to-read distance.
-__device__ __forceinline__ void acc_drain(f32x4 (&acc)[8][8]) {
-  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
-  acc_fence(acc);
-}
-// One block's accumulators moved to VGPRs where the epilogue uses them:
-// left to itself the compiler copied all 256 out of the AGPRs at once after
-// the K loop and spilled.
-__device__ __forceinline__ f32x4 acc_take(const f32x4& a) {
-  f32x4 v;
-  asm volatile("" : "=v"(v) : "0"(a));
-  return v;
-}
+//  * acc_fence() follows the zero fill, ahead of the prologue's loads, and
+//    acc_drain() follows the last MFMA (before the K tail and before the
+//    epilogue).
+__device__ __forceinline__ void mfma16(const bf16x8& a, const bf16x8& b, f32x4& c) { mfma16x16x32(b, a, c); }
 
 // s_waitcnt vmcnt(vm) lgkmcnt(lg) (expcnt unconstrained).
 template <int vm, int lg>

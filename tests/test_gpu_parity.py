@@ -292,6 +292,13 @@ SKINNY = [
     ({"T": 2}, "P(None, 'T')", "P('T', None)", 33, 2 * 128, 256),   # two row blocks, second has one row
     ({"T": 8}, "P(None, 'T')", "P('T', None)", 64, 8 * 256, 1024),  # two full row blocks
     ({"T": 4}, "P(None, 'T')", "P('T', None)", 48, 4 * 100, 296),   # two row blocks, ragged K and N
+    # 65..128 rows (past the split-J kernel: the tile kernel with ragged row tiles)
+    ({"T": 4}, "P(None, 'T')", "P('T', None)", 65, 4 * 128, 256),   # six blocks, the fifth has one row
+    ({"T": 2}, "P(None, 'T')", "P('T', None)", 96, 2 * 100, 296),   # six full blocks, ragged K and N
+    ({"T": 8}, "P(None, 'T')", "P('T', None)", 128, 8 * 256, 1024),  # eight full blocks, full column blocks
+    ({"T": 4}, "P(None, 'T')", "P('T', None)", 100, 4 * 96, 264),   # eight blocks, 3 K steps over 4 waves
+    ({"X": 2}, "P()", "P(None, 'X')", 97, 96, 2 * 128),              # case 1, 97 rows
+    ({"T": 2}, "P(None, 'T')", "P('T', None)", 127, 2 * 16, 128),   # K below one step
 ]
 
 
@@ -310,10 +317,11 @@ def test_skinny_shapes_bitexact(case):
     assert guard_intact(full, P.numel())
 
 
-@pytest.mark.parametrize("rows", [12, 40], ids=["rows12", "rows40"])
+@pytest.mark.parametrize("rows", [12, 40, 80, 128], ids=["rows12", "rows40", "rows80", "rows128"])
 @pytest.mark.parametrize("width", [256, 288], ids=["interior", "ragged"])
 def test_gelu_epilogue_skinny(width, rows):
-    """The GeLU(tanh) -> bfloat16 epilogue on the skinny path (M <= 64):
+    """The GeLU(tanh) -> bfloat16 epilogue for small batches (the split-J
+    kernel up to 64 rows, ragged row tiles of the tile kernel above):
     column blocks of a small batch, within the derived bound of the oracle's
     round_bf16(gelu(.))."""
     say("case: gelu epilogue skinny", width, rows)
@@ -569,6 +577,39 @@ def test_full_skinny_all_outputs(integer):
     else:
         worst = max(ref.rel_frobenius(Pn[u], parts[u]) for u in range(8))
         say("skinny partial rel err", worst)
+        assert worst <= REL_TOL
+        assert ref.rel_frobenius(out.cpu().numpy(), s) <= REL_TOL
+
+
+@pytest.mark.parametrize("integer", [False, True])
+def test_full_medium_batch(integer):
+    """A 128-row batch on the skinny workload's weights (8 x [128,3584] .
+    [3584,8192]): past the split-J kernel's 64 rows, the tile kernel with
+    half-empty row tiles at its full launch size, against the oracle's
+    partials and their sum."""
+    w = wl.get("skinny")
+    if integer:
+        w = wl.int_variant(w)
+    say("case: full medium batch", "int" if integer else "float")
+    rows = 128
+    X = wl.make_operand(w.operand("X"), shape=(rows, 28672))
+    A = wl.make_operand(w.operand("A"))
+    p, q = _plans(dict(w.mesh), w.operand("X").spec, w.operand("A").spec, rows, 28672, 8192)
+    full, P = run_partials(p, to_dev(X), to_dev(A))
+    out = torch.empty(rows, 8192, dtype=torch.float32, device=DEV)
+    sm.sm_reduce_partials(p, sm.buf(P), sm.buf(out), sm.SM_ALLREDUCE)
+    torch.cuda.synchronize()
+    assert guard_intact(full, P.numel())
+    parts = ref.partials(q, X, A)
+    (s,) = ref.allreduce(q, parts)
+    Pn = P.cpu().numpy()
+    if integer:
+        for u in range(8):
+            assert f32_bits_equal(Pn[u], parts[u]), u
+        assert f32_bits_equal(out.cpu().numpy(), s)
+    else:
+        worst = max(ref.rel_frobenius(Pn[u], parts[u]) for u in range(8))
+        say("medium partial rel err", worst)
         assert worst <= REL_TOL
         assert ref.rel_frobenius(out.cpu().numpy(), s) <= REL_TOL
 
