@@ -36,6 +36,9 @@ What each function follows, and what pins it (tests/test_oracle_*.py):
 
 Random-valued configurations have no page-printed outputs: their expected
 values are this oracle's, computed in fp64 from the exact stored inputs.
+
+tests/test_oracle_mutants.py plants plausible slips in copies of this
+module, the planner and oracle.c, and checks that some pin fails for each.
 """
 from __future__ import annotations
 

@@ -166,6 +166,30 @@ def test_allreduce_equals_reducescatter_then_allgather():
     np.testing.assert_array_equal(ar, A @ B)
 
 
+def test_two_dimensional_output_grid():
+    """Output blocks on a 2 x 2 grid (lingze.zone 'Case 1' C[I_X, K_Y]; 'Case 3'
+    generalisation with K sharded too): gathering the case-1 blocks, the
+    all-reduced blocks and the reduce-scattered row blocks must each give
+    the dense product (numpy), and coordinate y of group (bi, bk) owns rows
+    [bi m + y m/N, bi m + (y+1) m/N) of column block bk."""
+    A = _ints((16, 24), 45)
+    B = _ints((24, 12), 46)
+    D = A @ B
+    p1 = planner.plan({"X": 4, "Y": 2}, "A[I_X, J]", "B[J, K_Y]", 16, 24, 12)
+    assert p1.case == 1 and p1.c_grid == (4, 2)
+    np.testing.assert_array_equal(ref.gather(p1, ref.partials(p1, A, B)), D)
+    p3 = planner.plan({"X": 2, "Y": 2, "Z": 2}, "P('X', 'Y')", "P('Y', 'Z')", 16, 24, 12)
+    assert p3.case == 3 and p3.c_grid == (2, 2) and p3.n_partials == 2
+    parts = ref.partials(p3, A, B)
+    np.testing.assert_array_equal(ref.gather(p3, ref.allreduce(p3, parts)), D)
+    rs = ref.reduce_scatter(p3, parts)
+    np.testing.assert_array_equal(ref.gather_scattered(p3, rs), D)
+    for (g, y), blk in rs.items():
+        bi, bk = divmod(g, 2)
+        assert p3.rs_rows(g, y) == (bi * 8 + y * 4, 4)
+        np.testing.assert_array_equal(blk, D[bi * 8 + y * 4:bi * 8 + (y + 1) * 4, bk * 6:(bk + 1) * 6])
+
+
 def test_generalised_case3_groups():
     """lingze.zone 'Case 3', generalisation: A[I_X,J_Y].B[J_Y,K] -> partial
     sums of C[I_X,K]; group x's block is rows x*m.. of the dense product."""

@@ -90,6 +90,18 @@ def test_case4_diagonal_blocks_only():
     assert q.case == 1
 
 
+def test_case4_gathers_the_smaller_input():
+    """lingze.zone 'Case 4': the fix all-gathers one input, at a cost of V/W
+    with V the bytes of the gathered input; the cheaper choice is the
+    smaller one (ties: A, the page's own example)."""
+    for (I, J, K), want in (((4, 3, 8), "A"), ((8, 3, 4), "B"), ((4, 3, 4), "A")):
+        p = plan({"X": 2}, "A[I_X, J]", "B[J, K_X]", I, J, K)
+        assert p.case == 4 and p.gather_operand == want and p.gather_axes == ("X",)
+        q = planner.gathered(p)
+        assert q.case == 1
+        assert (q.a_copies, q.b_copies) == ((2, 1) if want == "A" else (1, 2))
+
+
 def test_case4_checked_before_j_cases():
     """Reading: an illegal output layout (case 4) takes precedence."""
     assert plan(XY, "A[I_Y, J_X]", "B[J_X, K_Y]", 8, 8, 8).case == 4
