@@ -300,7 +300,7 @@ def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default="downproj")
     ap.add_argument("--cpu-rows", type=int, default=6144, help="oracle sample size (output rows, unit by unit)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -340,17 +340,26 @@ def main() -> int:
         if p.kase == sm.SM_CASE3:
             reduce()
 
-    def back_to_back(fn, reps):
+    def back_to_back(fn, reps, warm_ms=100.0):
         """Average duration of one launch: `reps` launches queued back to back
-        on the kernels' stream between two HIP events. A ~5 ms spin kernel
-        goes first, so that all launches are queued before the GPU reaches
-        them and host-side call overhead never shows between short kernels.
-        Kernels under 0.2 ms are timed again over 10x as many launches."""
-        def once(n):
+        on the kernels' stream between two HIP events.
+
+        Kernels under 0.2 ms: a ~5 ms spin kernel goes first, so that all
+        launches are queued before the GPU reaches them and host-side call
+        overhead never shows between them; they are timed over 10x as many
+        launches. Longer kernels: about `warm_ms` of the same launches go
+        first instead, so that the timed ones run at the clock the board
+        settles at under this load (the first ~100 ms of back-to-back
+        matrix-core launches run a few percent slower)."""
+        def once(n, n_warm):
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             torch.cuda.synchronize()
-            with torch.cuda.stream(stream):
-                torch.cuda._sleep(10_000_000)
+            if n_warm:
+                for _ in range(n_warm):
+                    fn()
+            else:
+                with torch.cuda.stream(stream):
+                    torch.cuda._sleep(10_000_000)
             e0.record(stream)
             for _ in range(n):
                 fn()
@@ -359,8 +368,10 @@ def main() -> int:
             return e0.elapsed_time(e1) / n
 
         fn()
-        t = once(reps)
-        return once(10 * reps) if t < 0.2 else t
+        t = once(reps, 0)
+        if t < 0.2:
+            return once(10 * reps, 0)
+        return once(reps, int(warm_ms / t) + 1)
 
     def single_launches(fn, reps):
         """(median, min) ms of `reps` launches, each between its own two HIP
