@@ -9,8 +9,12 @@ the library's own flags and check the rules the kernel keeps instead:
     padding (three s_nop 7) have been issued;
   * no VALU instruction writes an MFMA's source VGPRs within 4 wait states
     before that MFMA;
-  * no scratch (spill) traffic anywhere in the kernel.
+  * no scratch (spill) traffic anywhere in the kernel;
+  * the float32 epilogue's 16-byte stores keep their streaming policy
+    (also inline assembly), and no instruction overwrites the data
+    registers of a store wider than 8 bytes in the next wait state.
 
+Each kernel is checked whole, up to its end (it has several s_endpgm).
 A change that breaks one of them would produce wrong results only on some
 runs, if at all, so it is caught here, on the host, before any GPU run.
 """
@@ -41,12 +45,13 @@ def kernels():
         assert r.returncode == 0, r.stderr[-2000:]
         text = open(out).read()
     found = {}
-    for m in re.finditer(r"^(" + KERNEL + r"\S+):[^\n]*\n(.*?)s_endpgm", text, re.S | re.M):
+    # the whole function: a kernel has several s_endpgm (early exits)
+    for m in re.finditer(r"^(" + KERNEL + r"\S+):[^\n]*\n(.*?)^\.Lfunc_end", text, re.S | re.M):
         lines = [l.strip() for l in m.group(2).split("\n")]
         ins = []
         for l in lines:
-            if l.endswith(":") or re.match(r"^\.LBB\S*:", l):
-                ins.append("<label>")  # a basic block starts
+            if l.endswith(":") or re.match(r"^\.LBB\S*:", l) or l.startswith("s_endpgm"):
+                ins.append("<label>")  # a basic block starts (or the wave ends)
             elif l and not l.startswith((";", ".")):
                 ins.append(l)
         found[m.group(1)] = ins
@@ -145,3 +150,36 @@ def test_no_valu_write_of_mfma_sources_just_before(kernels):
 def test_no_scratch_traffic(kernels):
     for name, ins in kernels.items():
         assert not [i for i in ins if i.startswith("scratch_")], name
+
+
+def _fp32_kernels(kernels):
+    # template arguments <OUT_BF16 = false, GELU>: float32 output
+    return {n: ins for n, ins in kernels.items() if "ILb0E" in n}
+
+
+def test_float32_tile_stores_stream(kernels):
+    """The float32 epilogue stores its 16-byte vectors with the streaming,
+    system-scope policy; a plain store here would leave the burst's dirty
+    lines in the L2 in the way of the next wave of tiles."""
+    fp32 = _fp32_kernels(kernels)
+    assert len(fp32) == 2
+    for name, ins in fp32.items():
+        st = [i for i in ins if i.startswith("global_store_dwordx4")]
+        assert sum(1 for i in st if i.endswith("nt sc0 sc1")) >= 64, name
+
+
+def test_store_data_not_overwritten_in_the_next_wait_state(kernels):
+    """A store of more than 8 bytes reads its data registers after issue:
+    the next instruction must not write them (one wait state, an s_nop or
+    any other instruction, must come first)."""
+    for name, ins in kernels.items():
+        body = [i for i in ins if i != "<label>"]
+        for k, i in enumerate(body[:-1]):
+            if not i.startswith(("global_store_dwordx3", "global_store_dwordx4",
+                                 "buffer_store_dwordx3", "buffer_store_dwordx4")):
+                continue
+            data = _regs(_operands(i)[1])
+            nxt = body[k + 1]
+            if nxt.startswith("s_") or not nxt.startswith("v_"):
+                continue
+            assert not (_regs(_operands(nxt)[0]) & data), (name, i, nxt)
