@@ -91,6 +91,11 @@ __device__ __forceinline__ void transpose8(const uint4 (&in)[8], uint4 (&out)[8]
 
 
 // Workgroup id -> (virtual tile row, tile column). A bijection on [0, T).
+// Each run of 256 workgroups (one wave of tiles, one per CU) covers a 16x16
+// block of tiles, each XCD a 4x8 part of it. Groups of 16 tile rows walk
+// their columns in alternating directions, so every wave shares the A or
+// the B panels of the wave before it while those may still sit in the
+// Infinity Cache: +0.5-1 % on multi-wave launches, same-box A/B.
 __device__ __forceinline__ void tile_of(int w, int T, int VR, int VC, int* vr, int* vc) {
   int t = w;
   const int chunk = w >> 8;
@@ -106,7 +111,7 @@ __device__ __forceinline__ void tile_of(int w, int T, int VR, int VC, int* vr, i
   const int rows = min(GM, VR - first);
   const int idx = t - group * GM * VC;
   *vr = first + idx % rows;
-  *vc = idx / rows;
+  *vc = (group & 1) ? VC - 1 - idx / rows : idx / rows;
 }
 
 // One 32x32 block of v_mfma_f32_32x32x16_bf16. TRANS puts the B fragment
