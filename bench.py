@@ -244,7 +244,49 @@ def measure_rows(back_to_back, cold, stream) -> dict:
                               sm.sm_reshard(mesh4, frm, to, I, J, sm.SM_BF16, q, bd4, stream)), 2 * 2.0 * I * J)
     rows["f4_alltoall_reshard"] = {"workload": f"bf16 [{I},{J}] A[I,J_X] -> A[I_X,J] on {{X:4}}",
                                    **rate("hbm", 2 * 2.0 * I * J, rs, rs_cold)}
+    rows["a7_skinny"] = measure_skinny(back_to_back, cold, stream)
     return rows
+
+
+def measure_skinny(back_to_back, cold, stream) -> dict:
+    """Row a7 on the skinny workload (X[16,28672] . A[28672,8192], J split
+    over {T:8}): the split-J kernel with the fused rank-ordered all-reduce
+    of its 8 partials (sm_local_gemm_reduce_ws), and, for comparison, the
+    split-J kernel alone plus sm_reduce_partials. HBM-bound: the
+    algorithmic bytes are A, X and the output once (471.2 MB); the 8 fp32
+    partials the kernel writes and re-reads through the workspace (8.4 MB)
+    are not counted."""
+    import torch
+
+    import local_shard_gemm_amd as sm
+    import workloads as wl
+
+    dev = torch.device("cuda:0")
+    w = wl.get("skinny")
+    X = wl.make_operand(w.operand("X")).to(dev)
+    A = wl.make_operand(w.operand("A")).to(dev)
+    B_, J = X.shape
+    K = A.shape[1]
+    p = sm.sm_plan(dict(w.mesh), w.operand("X").spec, w.operand("A").spec, B_, J, K)
+    ws = torch.zeros(sm.sm_gemm_reduce_workspace(p) // 4 + 1, dtype=torch.int32, device=dev)
+    out = torch.empty(B_, K, dtype=torch.float32, device=dev)
+    P = torch.empty(p.n_units, B_, K, dtype=torch.float32, device=dev)
+    bx, ba, bo, bp = sm.buf(X), sm.buf(A), sm.buf(out), sm.buf(P)
+    work = 2.0 * (B_ * J + J * K) + 4.0 * B_ * K
+    extra = 2 * 4.0 * p.n_units * B_ * K
+
+    def fused(q=ba):
+        sm.sm_local_gemm_reduce_ws(p, bx, q, bo, ws, sm.SM_ALLREDUCE, 0, p.n_groups, stream)
+
+    f = back_to_back(fused)
+    f_cold = cold(lambda i: (lambda q=(ba if i == 0 else sm.buf(A.clone())): fused(q)), work)
+    g = back_to_back(lambda: sm.sm_local_gemm(p, bx, ba, bp, sm.SM_EPI_STORE, 0, p.n_units, stream))
+    r = back_to_back(lambda: sm.sm_reduce_partials(p, bp, bo, sm.SM_ALLREDUCE, 0, p.n_groups, stream))
+    entry = rate("hbm", work, f, f_cold)
+    return {"workload": f"{w.name}: X[{B_},{J}] . A[{J},{K}], J split over {{T:{p.n_partials}}}, all-reduce",
+            "fused_gemm_reduce": {**entry, "partials_bytes_not_counted": extra},
+            "split_j_gemm_then_reduce_ms": round(g + r, 4),
+            "split_j_gemm_ms": round(g, 4), "reduce_ms": round(r, 4)}
 
 
 def source_digest(paths) -> str:

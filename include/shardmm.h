@@ -245,10 +245,51 @@ int32_t sm_reduce_partials(const sm_plan_t* plan, const sm_buf* partials,
  * A and B must use the global layout (block_stride 0). The result equals
  * sm_local_gemm + sm_reduce_partials up to fp32 summation order (bit for
  * bit on integer-valued inputs). Local products of at most 64 rows are
- * refused with SM_ERR_SHAPE (their split-J kernel needs the partials). */
+ * refused with SM_ERR_SHAPE: their split-J kernel needs a workspace
+ * (sm_local_gemm_reduce_ws). */
 int32_t sm_local_gemm_reduce(const sm_plan_t* plan, const sm_buf* A, const sm_buf* B,
                              const sm_buf* out, int32_t mode, int32_t group_begin,
                              int32_t group_count, void* stream);
+
+/* Bytes of device workspace sm_local_gemm_reduce_ws needs for group_count
+ * groups of a case-3 plan: 0 when the local products have more than 64
+ * rows, else the arrival counters followed by the N partials of each group
+ * (see below). Errors: SM_ERR_CASE unless case 3, SM_ERR_ARG for a
+ * group_count outside [1, n_groups]. */
+int32_t sm_gemm_reduce_workspace(const sm_plan_t* plan, int32_t group_count, int64_t* bytes);
+
+/* sm_local_gemm_reduce for every local-product height, with a
+ * caller-provided workspace (mbrenndoerfer.com "Row Parallelism": each rank
+ * forms Z_i = X_i A_i and the output is their sum Y = sum_i X_i A_i;
+ * semiaifoundry.com "The mechanism", step 4). Local products of more than
+ * 64 rows run exactly as in sm_local_gemm_reduce and leave the workspace
+ * untouched (it may be NULL then). Local products of at most 64 rows (a
+ * skinny batch) run the split-J streaming kernel with the reduction fused
+ * into it, in one launch per 64 units:
+ *  - every workgroup (one unit y of group g, one block of 256 output
+ *    columns) writes its partial P_{g,y} into the workspace and counts
+ *    itself in at the counter of its (group, column block);
+ *  - the workgroup that arrives last sums that block's N partials in rank
+ *    order, S_g = ((P_{g,0} + P_{g,1}) + ...) + P_{g,N-1}, writes the rows
+ *    to `out` as sm_local_gemm_reduce does (AR or RS, global or stacked),
+ *    and returns the counter to zero. No workgroup waits for another.
+ * Workspace (device memory, 256-byte aligned, workspace_bytes >=
+ * sm_gemm_reduce_workspace(plan, group_count)), owned by the caller:
+ *  - bytes [0, C): 32-bit arrival counters, C = 4 * group_count *
+ *    ceil(n / 256) rounded up to 256. They must be zero before the first
+ *    call (a zero-filled allocation); every call leaves them zero.
+ *  - bytes [C, ...): the partials, float32, stacked by (g - group_begin)
+ *    * N + y, each [m, ld] with ld = n rounded up to 4. After the call they
+ *    hold every unit's partial (bit for bit what sm_local_gemm stores).
+ * Calls that share a workspace must not overlap in time (same stream, or
+ * synchronised). Errors as sm_local_gemm_reduce; SM_ERR_SHAPE for a
+ * workspace too small or more than 64 partials per group; SM_ERR_ALIGN for
+ * a misaligned workspace; SM_ERR_ARG for NULL or non-device workspace
+ * memory when one is needed. */
+int32_t sm_local_gemm_reduce_ws(const sm_plan_t* plan, const sm_buf* A, const sm_buf* B,
+                                const sm_buf* out, int32_t mode, int32_t group_begin,
+                                int32_t group_count, void* workspace, int64_t workspace_bytes,
+                                void* stream);
 
 /* Sequence-parallel tail (ana-alekseeva.com "Sequence parallelism": the
  * all-reduce of a tensor-parallel block becomes a reduce-scatter, layer norm

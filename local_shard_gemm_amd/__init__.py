@@ -55,7 +55,7 @@ EXPORTED = (
     "sm_abi_version", "sm_plan_size", "sm_status_str", "sm_last_error", "sm_mesh_init",
     "sm_parse_spec", "sm_plan", "sm_rank_info", "sm_local_gemm", "sm_reduce_partials",
     "sm_gather_shards", "sm_plan_gathered", "sm_local_gemm_reduce", "sm_reduce_scatter_layernorm",
-    "sm_reshard",
+    "sm_reshard", "sm_gemm_reduce_workspace", "sm_local_gemm_reduce_ws",
 )
 
 
@@ -156,6 +156,11 @@ def load(path: str = LIB_PATH):
         lib.sm_plan_gathered.argtypes = [P(sm_plan_t), P(sm_plan_t)]
         lib.sm_local_gemm_reduce.restype = i32
         lib.sm_local_gemm_reduce.argtypes = [P(sm_plan_t), P(sm_buf), P(sm_buf), P(sm_buf), i32, i32, i32, vp]
+        lib.sm_gemm_reduce_workspace.restype = i32
+        lib.sm_gemm_reduce_workspace.argtypes = [P(sm_plan_t), i32, P(i64)]
+        lib.sm_local_gemm_reduce_ws.restype = i32
+        lib.sm_local_gemm_reduce_ws.argtypes = [P(sm_plan_t), P(sm_buf), P(sm_buf), P(sm_buf), i32, i32, i32, vp, i64,
+                                                vp]
         lib.sm_reduce_scatter_layernorm.restype = i32
         lib.sm_reduce_scatter_layernorm.argtypes = [P(sm_plan_t), P(sm_buf), P(sm_buf), vp, vp, ctypes.c_float,
                                                     i32, i32, vp]
@@ -290,6 +295,36 @@ def sm_local_gemm_reduce(plan: sm_plan_t, A, B, out, mode: int = SM_ALLREDUCE, g
     a, b, o = _as_buf(A), _as_buf(B), _as_buf(out)
     _check(load().sm_local_gemm_reduce(ctypes.byref(plan), ctypes.byref(a), ctypes.byref(b), ctypes.byref(o),
                                        mode, group_begin, group_count, _stream(stream)))
+
+
+def sm_gemm_reduce_workspace(plan: sm_plan_t, group_count: Optional[int] = None) -> int:
+    """Workspace bytes sm_local_gemm_reduce_ws needs for ``group_count``
+    groups (all of the plan's by default)."""
+    if group_count is None:
+        group_count = plan.n_groups
+    n = ctypes.c_int64()
+    _check(load().sm_gemm_reduce_workspace(ctypes.byref(plan), group_count, ctypes.byref(n)))
+    return n.value
+
+
+def sm_local_gemm_reduce_ws(plan: sm_plan_t, A, B, out, workspace, mode: int = SM_ALLREDUCE, group_begin: int = 0,
+                            group_count: Optional[int] = None, stream=None) -> None:
+    """``workspace``: a device tensor (zero-filled before its first use; each
+    call leaves its counters zero) of at least sm_gemm_reduce_workspace
+    bytes, a (pointer, bytes) pair, or None when the plan needs none."""
+    if group_count is None:
+        group_count = plan.n_groups - group_begin
+    a, b, o = _as_buf(A), _as_buf(B), _as_buf(out)
+    if workspace is None:
+        wp, wn = ctypes.c_void_p(0), 0
+    elif isinstance(workspace, tuple):
+        wp, wn = ctypes.c_void_p(int(workspace[0])), int(workspace[1])
+    else:
+        if not workspace.is_contiguous():
+            raise ValueError("the workspace must be a contiguous tensor")
+        wp, wn = ctypes.c_void_p(workspace.data_ptr()), workspace.numel() * workspace.element_size()
+    _check(load().sm_local_gemm_reduce_ws(ctypes.byref(plan), ctypes.byref(a), ctypes.byref(b), ctypes.byref(o),
+                                          mode, group_begin, group_count, wp, wn, _stream(stream)))
 
 
 def sm_reduce_scatter_layernorm(plan: sm_plan_t, partials, out, gamma=None, beta=None, eps: float = 1e-5,

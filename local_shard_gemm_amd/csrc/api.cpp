@@ -13,6 +13,10 @@
 #include "kernels.h"
 
 namespace shardmm {
+ReduceWorkspace reduce_workspace(const sm_plan_t& p, int64_t groups);
+}  // namespace shardmm
+
+namespace shardmm {
 
 static const char* dtype_name(int32_t d) { return d == SM_BF16 ? "bfloat16" : d == SM_F32 ? "float32" : "unknown"; }
 
@@ -408,9 +412,28 @@ extern "C" int32_t sm_gather_shards(const sm_plan_t* plan, int32_t what, const s
   return run_jobs(jobs, 1, static_cast<int32_t>(esz), static_cast<hipStream_t>(stream), "sm_gather_shards launch");
 }
 
-extern "C" int32_t sm_local_gemm_reduce(const sm_plan_t* plan, const sm_buf* A, const sm_buf* B, const sm_buf* out,
-                                        int32_t mode, int32_t group_begin, int32_t group_count, void* stream) {
-  clear_error();
+namespace shardmm {
+
+ReduceWorkspace reduce_workspace(const sm_plan_t& p, int64_t groups) {
+  ReduceWorkspace w{};
+  const int64_t m = p.c_local[0], n = p.c_local[1];
+  if (m > kSkinnyMaxM) return w;  // the tile kernel reduces without a workspace
+  w.n_colblk = static_cast<int32_t>((n + kSkinnyCols - 1) / kSkinnyCols);
+  w.ldp = (n + 3) / 4 * 4;
+  w.counter_bytes = (groups * w.n_colblk * 4 + 255) / 256 * 256;
+  w.part_bytes = groups * p.n_partials * m * w.ldp * 4;
+  return w;
+}
+
+// Local products of a case-3 plan and their rank-ordered reduction, for
+// sm_local_gemm_reduce (ws == nullptr), sm_local_gemm_reduce_ws and the
+// no-allocation entry point. Products of more than 64 rows: one tile-kernel
+// launch per batch of groups, K = the group's whole J, no workspace.
+// Skinny products: the split-J kernel with the fused reduction, whose
+// counters and partials live in `ws` (ws_bytes long).
+int32_t gemm_reduce_impl(const sm_plan_t* plan, const sm_buf* A, const sm_buf* B, const sm_buf* out, int32_t mode,
+                         int32_t group_begin, int32_t group_count, void* ws, int64_t ws_bytes, hipStream_t s,
+                         const char* where) {
   int32_t st = check_plan(plan);
   if (st) return st;
   const sm_plan_t& p = *plan;
@@ -430,10 +453,15 @@ extern "C" int32_t sm_local_gemm_reduce(const sm_plan_t* plan, const sm_buf* A, 
   if (B->ld < p.K) return fail(SM_ERR_SHAPE, "B: global layout needs ld >= K");
   const int64_t m = p.c_local[0], n = p.c_local[1], kfull = p.J;
   const int32_t N = p.n_partials;
-  if (m <= kSkinnyMaxM) return fail(SM_ERR_SHAPE, "skinny products reduce through sm_reduce_partials");
+  const bool skinny = m <= kSkinnyMaxM;
+  if (skinny && !ws)
+    return fail(SM_ERR_SHAPE, "local products of at most 64 rows reduce through a workspace "
+                              "(sm_local_gemm_reduce_ws)");
   if (m > INT32_MAX / 2 || n > INT32_MAX / 2 || kfull > INT32_MAX / 2) return fail(SM_ERR_SHAPE, "shape too large");
   if (((m + kTileM - 1) / kTileM) * ((n + kTileN - 1) / kTileN) * kMaxUnitsPerLaunch > INT32_MAX)
     return fail(SM_ERR_SHAPE, "too many output tiles for one launch grid");
+  if (skinny && N > kMaxUnitsPerLaunch)
+    return fail(SM_ERR_SHAPE, "the fused split-J reduction takes at most 64 partials per group");
   const bool rs = mode == SM_REDUCESCATTER;
   if (rs && m % N) return fail(SM_ERR_INDIVISIBLE, "rows of a block do not split N ways");
   const int64_t orows = rs ? m / N : m;
@@ -442,12 +470,20 @@ extern "C" int32_t sm_local_gemm_reduce(const sm_plan_t* plan, const sm_buf* A, 
   } else if ((st = check_stacked(out, orows, n, "out"))) {
     return st;
   }
+  ReduceWorkspace W{};
+  if (skinny) {
+    W = reduce_workspace(p, group_count);
+    if (reinterpret_cast<uintptr_t>(ws) % 256) return fail(SM_ERR_ALIGN, "workspace not 256-byte aligned");
+    if (ws_bytes < W.counter_bytes + W.part_bytes)
+      return fail(SM_ERR_SHAPE, "workspace of " + std::to_string(ws_bytes) + " bytes, the call needs " +
+                                    std::to_string(W.counter_bytes + W.part_bytes));
+  }
 
   GemmLaunch L;
   std::memset(&L, 0, sizeof L);
   L.M = static_cast<int32_t>(m);
   L.N = static_cast<int32_t>(n);
-  L.K = static_cast<int32_t>(kfull);
+  L.K = static_cast<int32_t>(skinny ? p.a_local[1] : kfull);
   L.tiles_m = static_cast<int32_t>((m + kTileM - 1) / kTileM);
   L.tiles_n = static_cast<int32_t>((n + kTileN - 1) / kTileN);
   L.lda = A->ld;
@@ -466,6 +502,8 @@ extern "C" int32_t sm_local_gemm_reduce(const sm_plan_t* plan, const sm_buf* A, 
     GemmUnitPtrs ptrs;
   };
   std::vector<Item> items;
+  std::vector<float*> group_out;
+  bool out_vec = n % 4 == 0 && out->ld % 4 == 0 && L.split_stride % 4 == 0;
   for (int32_t g = group_begin; g < group_begin + group_count; ++g) {
     // Rank order y = 0..N-1 covers J contiguously in both operands.
     UnitView v;
@@ -489,30 +527,111 @@ extern "C" int32_t sm_local_gemm_reduce(const sm_plan_t* plan, const sm_buf* A, 
       }
       coff = static_cast<int64_t>(c0);  // bounded by the checks above
     }
-    Item it;
-    it.b_id = v.b_block[1];
-    it.a_row = v.a_block[0];
-    it.ptrs.a = static_cast<const uint16_t*>(A->ptr) + ra.off();
-    it.ptrs.b = static_cast<const uint16_t*>(B->ptr) + rb.off();
-    it.ptrs.c = static_cast<float*>(out->ptr) + coff;
+    float* c = static_cast<float*>(out->ptr) + coff;
+    if (reinterpret_cast<uintptr_t>(c) % 16) {
+      L.vec_c = 0;  // float32 partial sums
+      out_vec = false;
+    }
     if (!b_rows_padded(B, rb)) L.vec_ok = 0;
-    if (reinterpret_cast<uintptr_t>(it.ptrs.a) % 16 || reinterpret_cast<uintptr_t>(it.ptrs.b) % 16) L.vec_ok = 0;
-    if (reinterpret_cast<uintptr_t>(it.ptrs.c) % 16) L.vec_c = 0;  // float32 partial sums
-    items.push_back(it);
+    if (skinny) {
+      // the split-J kernel runs the N units of the group, each on its own
+      // J slice: A view [m, k_local] at column y * k_local, B view
+      // [k_local, n] at row y * k_local
+      group_out.push_back(c);
+      const int64_t kl = p.a_local[1];
+      for (int32_t y = 0; y < N; ++y) {
+        Item it;
+        it.b_id = 0;
+        it.a_row = 0;
+        it.ptrs.a = static_cast<const uint16_t*>(A->ptr) + ra.off() + y * kl;
+        it.ptrs.b = static_cast<const uint16_t*>(B->ptr) + rb.off() + static_cast<int64_t>(y) * kl * B->ld;
+        it.ptrs.c = nullptr;
+        if (reinterpret_cast<uintptr_t>(it.ptrs.a) % 16 || reinterpret_cast<uintptr_t>(it.ptrs.b) % 16) L.vec_ok = 0;
+        items.push_back(it);
+      }
+    } else {
+      Item it;
+      it.b_id = v.b_block[1];
+      it.a_row = v.a_block[0];
+      it.ptrs.a = static_cast<const uint16_t*>(A->ptr) + ra.off();
+      it.ptrs.b = static_cast<const uint16_t*>(B->ptr) + rb.off();
+      it.ptrs.c = c;
+      if (reinterpret_cast<uintptr_t>(it.ptrs.a) % 16 || reinterpret_cast<uintptr_t>(it.ptrs.b) % 16) L.vec_ok = 0;
+      items.push_back(it);
+    }
   }
   if ((st = check_device_memory(A->ptr, "A")) || (st = check_device_memory(B->ptr, "B")) ||
       (st = check_device_memory(out->ptr, "out")))
     return st;
+  if (skinny && (st = check_device_memory(ws, "workspace"))) return st;
+
+  if (skinny) {
+    uint32_t* counters = static_cast<uint32_t*>(ws);
+    float* parts = reinterpret_cast<float*>(static_cast<char*>(ws) + W.counter_bytes);
+    SkinnyReduce R;
+    std::memset(&R, 0, sizeof R);
+    R.part_stride = m * W.ldp;
+    R.ldp = W.ldp;
+    R.n_colblk = W.n_colblk;
+    R.n_partials = N;
+    R.split_rows = L.split_rows;
+    R.split_stride = L.split_stride;
+    R.ldo = out->ld;
+    R.vec_out = out_vec ? 1 : 0;
+    const int32_t groups_per_launch = kMaxUnitsPerLaunch / N;
+    for (int32_t g0 = 0; g0 < group_count; g0 += groups_per_launch) {
+      const int32_t gc = std::min(groups_per_launch, group_count - g0);
+      L.n_units = gc * N;
+      for (int32_t i = 0; i < gc * N; ++i) L.u[i] = items[static_cast<size_t>(g0) * N + i].ptrs;
+      for (int32_t i = 0; i < gc; ++i) R.out[i] = group_out[g0 + i];
+      R.part = parts + static_cast<int64_t>(g0) * N * R.part_stride;
+      R.counters = counters + static_cast<int64_t>(g0) * W.n_colblk;
+      hipError_t e = launch_gemm_skinny_reduce(L, R, s);
+      if (e != hipSuccess) return hip_fail(e, where);
+    }
+    return SM_OK;
+  }
+
   std::stable_sort(items.begin(), items.end(), [](const Item& x, const Item& y) {
     return x.b_id != y.b_id ? x.b_id < y.b_id : x.a_row < y.a_row;
   });
-  hipStream_t s = static_cast<hipStream_t>(stream);
   for (size_t first = 0; first < items.size(); first += kMaxUnitsPerLaunch) {
     const size_t cnt = std::min(items.size() - first, static_cast<size_t>(kMaxUnitsPerLaunch));
     L.n_units = static_cast<int32_t>(cnt);
     for (size_t i = 0; i < cnt; ++i) L.u[i] = items[first + i].ptrs;
     hipError_t e = launch_gemm_mfma(L, s);
-    if (e != hipSuccess) return hip_fail(e, "sm_local_gemm_reduce launch");
+    if (e != hipSuccess) return hip_fail(e, where);
   }
   return SM_OK;
+}
+
+}  // namespace shardmm
+
+extern "C" int32_t sm_local_gemm_reduce(const sm_plan_t* plan, const sm_buf* A, const sm_buf* B, const sm_buf* out,
+                                        int32_t mode, int32_t group_begin, int32_t group_count, void* stream) {
+  clear_error();
+  return gemm_reduce_impl(plan, A, B, out, mode, group_begin, group_count, nullptr, 0,
+                          static_cast<hipStream_t>(stream), "sm_local_gemm_reduce launch");
+}
+
+extern "C" int32_t sm_gemm_reduce_workspace(const sm_plan_t* plan, int32_t group_count, int64_t* bytes) {
+  clear_error();
+  int32_t st = check_plan(plan);
+  if (st) return st;
+  if (!bytes) return fail(SM_ERR_ARG, "NULL bytes");
+  if (plan->kase != SM_CASE3) return fail(SM_ERR_CASE, "only case-3 plans have partial sums to reduce");
+  if (group_count < 1 || group_count > plan->n_groups) return fail(SM_ERR_ARG, "group_count outside [1, n_groups]");
+  const ReduceWorkspace w = reduce_workspace(*plan, group_count);
+  *bytes = w.counter_bytes + w.part_bytes;
+  return SM_OK;
+}
+
+extern "C" int32_t sm_local_gemm_reduce_ws(const sm_plan_t* plan, const sm_buf* A, const sm_buf* B,
+                                           const sm_buf* out, int32_t mode, int32_t group_begin,
+                                           int32_t group_count, void* workspace, int64_t workspace_bytes,
+                                           void* stream) {
+  clear_error();
+  if (plan && plan->c_local[0] <= kSkinnyMaxM && !workspace) return fail(SM_ERR_ARG, "NULL workspace");
+  return gemm_reduce_impl(plan, A, B, out, mode, group_begin, group_count, workspace, workspace_bytes,
+                          static_cast<hipStream_t>(stream), "sm_local_gemm_reduce_ws launch");
 }

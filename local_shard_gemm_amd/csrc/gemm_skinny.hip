@@ -26,8 +26,17 @@
 //  * The next step's 8 loads are in flight while a step's MFMAs run.
 //  * The 4 wave partials are added in LDS in wave order (a fixed order, so
 //    the result is deterministic), 32 rows per pass, and stored once.
+//  * Fused reduction (sm_local_gemm_reduce_ws): the sum over the N ranks'
+//    partials, Y = sum_i X_i A_i, runs in the same launch. Each workgroup
+//    stores its partial block into the caller's workspace and counts itself
+//    in at its (group, column block) counter; the workgroup that arrives
+//    last adds the N partials of that block in rank order and writes the
+//    finished rows, then returns the counter to zero. Arrival order never
+//    changes the result: the sum is always ((P_0 + P_1) + ...) + P_{N-1}.
 #include "device_math.h"
 #include "kernels.h"
+
+#include <algorithm>
 
 namespace shardmm {
 namespace {
@@ -110,8 +119,76 @@ __device__ __forceinline__ void load_step(StepRegs<RB>& r, const uint16_t* X, in
   }
 }
 
-template <bool EDGE, bool OUT_BF16, bool GELU, int RB, int PROWS>
-__global__ __launch_bounds__(NT) void gemm_skinny_kernel(const GemmLaunch L) {
+// The workgroup that arrives last at its (group, column block) counter
+// sums the group's N partials of that block in rank order, ((P_0 + P_1) +
+// P_2) + ..., and writes the finished rows (split into the reduce-scatter
+// owners' blocks when split_rows < M). Partials of other workgroups were
+// written before their release fences; the caller issued the acquire.
+__device__ __forceinline__ void finish_block(const SkinnyReduce& R, int group, int M, int N, int n0) {
+  const int tid = threadIdx.x;
+  const int nsum = R.n_partials;
+  const float* base = R.part + static_cast<int64_t>(group) * nsum * R.part_stride;
+  float* out = R.out[group];
+  const int cols = min(COLS, N - n0);
+  auto dst_of = [&](int row) -> float* {
+    return out + (row / R.split_rows) * R.split_stride + static_cast<int64_t>(row % R.split_rows) * R.ldo;
+  };
+  if (R.vec_out) {
+    // cols is a multiple of 4: N is, and n0 is a multiple of 256
+    const int c4n = cols >> 2;
+    const int total = M * c4n;
+    constexpr int U = 4, YB = 8;  // one round of loads for 16 rows
+    for (int q0 = tid; q0 < total; q0 += NT * U) {
+      float4 acc[U];
+      for (int y0 = 0; y0 < nsum; y0 += YB) {
+        float4 v[YB][U];
+#pragma unroll
+        for (int i = 0; i < YB; ++i)
+#pragma unroll
+          for (int u = 0; u < U; ++u) {
+            const int q = q0 + u * NT;
+            if (y0 + i < nsum && q < total) {
+              const int row = q / c4n, c = n0 + 4 * (q - row * c4n);
+              v[i][u] = *reinterpret_cast<const float4*>(base + (y0 + i) * R.part_stride + row * R.ldp + c);
+            }
+          }
+#pragma unroll
+        for (int i = 0; i < YB; ++i)
+#pragma unroll
+          for (int u = 0; u < U; ++u) {
+            if (y0 + i >= nsum) continue;
+            if (y0 + i == 0) {
+              acc[u] = v[i][u];
+            } else {
+              acc[u].x += v[i][u].x;
+              acc[u].y += v[i][u].y;
+              acc[u].z += v[i][u].z;
+              acc[u].w += v[i][u].w;
+            }
+          }
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int q = q0 + u * NT;
+        if (q < total) {
+          const int row = q / c4n, c = n0 + 4 * (q - row * c4n);
+          *reinterpret_cast<float4*>(dst_of(row) + c) = acc[u];
+        }
+      }
+    }
+  } else {
+    for (int q = tid; q < M * cols; q += NT) {
+      const int row = q / cols, c = n0 + (q - row * cols);
+      const float* p = base + row * R.ldp + c;
+      float sum = p[0];
+      for (int y = 1; y < nsum; ++y) sum += p[y * R.part_stride];
+      dst_of(row)[c] = sum;
+    }
+  }
+}
+
+template <bool EDGE, bool OUT_BF16, bool GELU, int RB, int PROWS, bool FUSED>
+__global__ __launch_bounds__(NT) void gemm_skinny_kernel(const GemmLaunch L, const SkinnyReduce R) {
   __shared__ float red[WAVES][PROWS][COLS];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int h = lane >> 5, j = lane & 31;
@@ -153,6 +230,9 @@ __global__ __launch_bounds__(NT) void gemm_skinny_kernel(const GemmLaunch L) {
 
   // Output of MFMA (b, c), register v: row 32b + 8(v/4) + 4h + v%4, column
   // n0 + 8j + c. One reduction pass per row block, rows past M skipped.
+  // Fused: the unit's partial goes to the workspace instead of the output.
+  float* part = nullptr;
+  if constexpr (FUSED) part = R.part + blockIdx.y * R.part_stride;
 #pragma unroll
   for (int b = 0; b < RB; ++b) {
     const int rows = min(PROWS, M - 32 * b);
@@ -172,41 +252,95 @@ __global__ __launch_bounds__(NT) void gemm_skinny_kernel(const GemmLaunch L) {
       for (int w = 1; w < WAVES; ++w) sum += red[w][m][col];
       const int n = n0 + col;
       if (n < N) {
-        if (GELU) sum = gelu_tanh_f32(sum);
-        const int64_t off = static_cast<int64_t>(32 * b + m) * L.ldc + n;
-        if (OUT_BF16)
-          static_cast<uint16_t*>(U.c)[off] = bf16_rne(sum);
-        else
-          static_cast<float*>(U.c)[off] = sum;
+        if constexpr (FUSED) {
+          // agent-scope stores write through to where every XCD reads
+          // them, so the release below has no dirty partial lines to flush
+          __hip_atomic_store(part + static_cast<int64_t>(32 * b + m) * R.ldp + n, sum, __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+        } else {
+          if (GELU) sum = gelu_tanh_f32(sum);
+          const int64_t off = static_cast<int64_t>(32 * b + m) * L.ldc + n;
+          if (OUT_BF16)
+            static_cast<uint16_t*>(U.c)[off] = bf16_rne(sum);
+          else
+            static_cast<float*>(U.c)[off] = sum;
+        }
       }
     }
   }
+
+  if constexpr (FUSED) {
+    // Arrival: every thread's partial stores are ordered before the
+    // workgroup barrier (workgroup-scope release), and one thread counts the
+    // workgroup in with a vector atomic that releases at device scope, so
+    // the whole workgroup's stores happen before the count. The last of the
+    // N arrivals acquires (every thread) and finishes the block. No
+    // workgroup ever waits for another. One device-scope release (an L2
+    // write-back) per workgroup, not one per wave: on the [16, 28672] x
+    // [28672, 8192] split over 8 ranks the launch took 94 us with one per
+    // wave and 77 us like this (split-J kernel + separate reduce: 75 us).
+    __shared__ int s_last;
+    const int group = blockIdx.y / R.n_partials;
+    uint32_t* counter = R.counters + group * R.n_colblk + blockIdx.x;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __syncthreads();
+    if (tid == 0) {
+      const uint32_t before = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+      const int last = before == static_cast<uint32_t>(R.n_partials - 1);
+      // every arrival of this launch has happened: the counter goes back to
+      // zero for the next call
+      if (last) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      s_last = last;
+    }
+    __syncthreads();
+    if (!s_last) return;
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    finish_block(R, group, M, N, n0);
+  }
 }
 
-template <bool OUT_BF16, bool GELU, int RB, int PROWS>
-hipError_t launch_rb(const GemmLaunch& L, hipStream_t s) {
+__global__ __launch_bounds__(NT) void zero_words_kernel(uint32_t* p, int64_t n) {
+  for (int64_t i = blockIdx.x * static_cast<int64_t>(NT) + threadIdx.x; i < n; i += static_cast<int64_t>(gridDim.x) * NT)
+    p[i] = 0u;
+}
+
+template <bool OUT_BF16, bool GELU, int RB, int PROWS, bool FUSED>
+hipError_t launch_rb(const GemmLaunch& L, const SkinnyReduce& R, hipStream_t s) {
   const bool edge = (L.N % COLS) != 0 || (L.K % KSTEP) != 0 || !L.vec_ok;
   dim3 grid((L.N + COLS - 1) / COLS, L.n_units);
   if (edge)
-    hipLaunchKernelGGL((gemm_skinny_kernel<true, OUT_BF16, GELU, RB, PROWS>), grid, dim3(NT), 0, s, L);
+    hipLaunchKernelGGL((gemm_skinny_kernel<true, OUT_BF16, GELU, RB, PROWS, FUSED>), grid, dim3(NT), 0, s, L, R);
   else
-    hipLaunchKernelGGL((gemm_skinny_kernel<false, OUT_BF16, GELU, RB, PROWS>), grid, dim3(NT), 0, s, L);
+    hipLaunchKernelGGL((gemm_skinny_kernel<false, OUT_BF16, GELU, RB, PROWS, FUSED>), grid, dim3(NT), 0, s, L, R);
   return hipGetLastError();
 }
 
-template <bool OUT_BF16, bool GELU>
-hipError_t launch_variant(const GemmLaunch& L, hipStream_t s) {
-  if (L.M <= 16) return launch_rb<OUT_BF16, GELU, 1, 16>(L, s);
-  if (L.M <= 32) return launch_rb<OUT_BF16, GELU, 1, 32>(L, s);
-  return launch_rb<OUT_BF16, GELU, 2, 32>(L, s);
+template <bool OUT_BF16, bool GELU, bool FUSED>
+hipError_t launch_variant(const GemmLaunch& L, const SkinnyReduce& R, hipStream_t s) {
+  if (L.M <= 16) return launch_rb<OUT_BF16, GELU, 1, 16, FUSED>(L, R, s);
+  if (L.M <= 32) return launch_rb<OUT_BF16, GELU, 1, 32, FUSED>(L, R, s);
+  return launch_rb<OUT_BF16, GELU, 2, 32, FUSED>(L, R, s);
 }
 
 }  // namespace
 
 hipError_t launch_gemm_skinny(const GemmLaunch& L, hipStream_t s) {
+  SkinnyReduce none{};
   if (L.out_bf16)
-    return L.epilogue == kEpiGelu ? launch_variant<true, true>(L, s) : launch_variant<true, false>(L, s);
-  return L.epilogue == kEpiGelu ? launch_variant<false, true>(L, s) : launch_variant<false, false>(L, s);
+    return L.epilogue == kEpiGelu ? launch_variant<true, true, false>(L, none, s)
+                                  : launch_variant<true, false, false>(L, none, s);
+  return L.epilogue == kEpiGelu ? launch_variant<false, true, false>(L, none, s)
+                                : launch_variant<false, false, false>(L, none, s);
+}
+
+hipError_t launch_gemm_skinny_reduce(const GemmLaunch& L, const SkinnyReduce& R, hipStream_t s) {
+  return launch_variant<false, false, true>(L, R, s);
+}
+
+hipError_t launch_zero_words(uint32_t* p, int64_t n, hipStream_t s) {
+  const int64_t blocks = std::min<int64_t>((n + NT - 1) / NT, 1024);
+  hipLaunchKernelGGL(zero_words_kernel, dim3(static_cast<unsigned>(std::max<int64_t>(blocks, 1))), dim3(NT), 0, s, p, n);
+  return hipGetLastError();
 }
 
 }  // namespace shardmm

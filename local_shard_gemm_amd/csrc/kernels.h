@@ -59,8 +59,33 @@ struct RowLaunch {
   RowJob jobs[kMaxJobsPerLaunch];
 };
 
+// Rank-ordered reduction fused into the skinny split-J kernel. Every
+// workgroup (one unit, one block of 256 output columns) writes its unit's
+// partial block into the workspace and counts itself in at the counter of
+// its (group, column block); the workgroup that arrives last sums the
+// group's N partials in rank order and writes the finished rows. Units of a
+// launch are ordered group-major (unit = group * N + y).
+struct SkinnyReduce {
+  float* part;            // partial of launch unit i at part + i * part_stride
+  int64_t part_stride;    // elements between two units' partials
+  int64_t ldp;            // leading dimension of a partial
+  uint32_t* counters;     // [groups of the launch][n_colblk], zero on entry, left zero
+  int32_t n_colblk;       // column blocks per unit (grid x)
+  int32_t n_partials;     // N
+  int32_t split_rows;     // output row r -> out + (r / split_rows) * split_stride + (r % split_rows) * ldo
+  int32_t vec_out;        // 1: 16-byte vectors for every partial and output row
+  int64_t split_stride;
+  int64_t ldo;
+  float* out[kMaxUnitsPerLaunch];  // finished block of launch group g
+};
+
 hipError_t launch_gemm_mfma(const GemmLaunch& L, hipStream_t s);
 hipError_t launch_gemm_skinny(const GemmLaunch& L, hipStream_t s);
+// The skinny kernel with the fused reduction (float32 store epilogue only).
+hipError_t launch_gemm_skinny_reduce(const GemmLaunch& L, const SkinnyReduce& R, hipStream_t s);
+// Zero `n` 32-bit words (a fill kernel, so that the call can sit in a
+// captured graph).
+hipError_t launch_zero_words(uint32_t* p, int64_t n, hipStream_t s);
 hipError_t launch_rows(const RowLaunch& L, hipStream_t s);
 // Host side: launch row jobs (rank-ordered sums when n_sum > 1, copies when
 // n_sum == 1) in batches of kMaxJobsPerLaunch; returns an sm_status.
@@ -75,7 +100,18 @@ constexpr int kLayerNormMaxCols = 32768;
 
 // Tile sizes of the MFMA kernel (host side uses them for the grid).
 constexpr int kTileM = 256, kTileN = 256, kTileK = 64;
-// Rows handled by the skinny split-J kernel.
+// Rows handled by the skinny split-J kernel, and its output columns per
+// workgroup.
 constexpr int kSkinnyMaxM = 64;
+constexpr int kSkinnyCols = 256;
+
+// Workspace of a fused skinny reduction (sm_local_gemm_reduce_ws): arrival
+// counters (one 32-bit word per group and column block, rounded up to 256
+// bytes), then the groups' N partials, each [M, ldp] float32.
+struct ReduceWorkspace {
+  int64_t counter_bytes, part_bytes, ldp;
+  int32_t n_colblk;
+};
+
 
 }  // namespace shardmm

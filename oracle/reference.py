@@ -284,6 +284,18 @@ def round_bf16(x: np.ndarray) -> np.ndarray:
     return out
 
 
+def mlp_hidden(plan1: Plan, X, W1, rows=None) -> np.ndarray:
+    """First layer of the Megatron MLP: H_u = round_bf16(gelu(X W1_u)) for
+    each column block u of W1 (GeLU applies per column block, since it is
+    elementwise), concatenated into [rows, F] bfloat16 bit patterns."""
+    assert plan1.case == 1
+    hs = []
+    for u in range(plan1.n_units):
+        y = unit_partial(plan1, X, W1, u, rows)
+        hs.append(round_bf16(gelu_tanh(y)))
+    return np.concatenate(hs, axis=1) if len(hs) > 1 else hs[0]
+
+
 def mlp_chain(plan1: Plan, plan2: Plan, X, W1, W2, rows=None):
     """Megatron MLP: column-split W1, GeLU on each column block, row-split W2.
 
@@ -292,11 +304,7 @@ def mlp_chain(plan1: Plan, plan2: Plan, X, W1, W2, rows=None):
     ``rows`` restricts the computation to a sample of output rows.
     """
     assert plan1.case == 1 and plan2.case == 3
-    hs = []
-    for u in range(plan1.n_units):
-        y = unit_partial(plan1, X, W1, u, rows)
-        hs.append(round_bf16(gelu_tanh(y)))
-    H = np.concatenate(hs, axis=1) if len(hs) > 1 else hs[0]
+    H = mlp_hidden(plan1, X, W1, rows)
     zs = []
     Hk = H.shape[1] // plan2.n_partials
     for u in range(plan2.n_units):

@@ -295,6 +295,41 @@ def test_fused_reduce_validation():
     assert _err(sm.sm_local_gemm_reduce, q, _fb(96, dt=BF), B, out, sm.SM_REDUCESCATTER) == sm.SM_ERR_INDIVISIBLE
 
 
+def test_skinny_fused_reduce_workspace_and_validation():
+    """Workspace size of the fused split-J reduction (counters rounded up to
+    256 bytes, then N partials [m, ld] per group, ld = n rounded up to 4),
+    and the host checks of sm_local_gemm_reduce_ws before any launch."""
+    sk = sm.sm_plan({"T": 8}, "P(None, 'T')", "P('T', None)", 16, 28672, 8192)
+    assert sm.sm_gemm_reduce_workspace(sk) == 256 + 8 * 16 * 8192 * 4
+    g2 = sm.sm_plan({"X": 2, "T": 4}, "P('X', 'T')", "P('T', None)", 48, 512, 300)
+    assert sm.sm_gemm_reduce_workspace(g2, 1) == 256 + 4 * 24 * 300 * 4
+    assert sm.sm_gemm_reduce_workspace(g2) == 256 + 2 * 4 * 24 * 300 * 4
+    big = sm.sm_plan({"T": 2}, "P(None, 'T')", "P('T', None)", 65, 128, 64)  # tile kernel: none needed
+    assert sm.sm_gemm_reduce_workspace(big) == 0
+    assert _err(sm.sm_gemm_reduce_workspace, sk, 2) == sm.SM_ERR_ARG
+    assert _err(sm.sm_gemm_reduce_workspace, sm.sm_plan({"X": 2}, "P('X', None)", "P()", 64, 128, 64)) \
+        == sm.SM_ERR_CASE
+    X, A, out = _fb(28672, dt=BF), _fb(8192, dt=BF), _fb(8192)
+    need = sm.sm_gemm_reduce_workspace(sk)
+    ws = (FAKE, need)
+    assert _err(sm.sm_local_gemm_reduce_ws, sk, X, A, out, None) == sm.SM_ERR_ARG
+    assert _err(sm.sm_local_gemm_reduce_ws, sk, X, A, out, (FAKE, need - 4)) == sm.SM_ERR_SHAPE
+    assert _err(sm.sm_local_gemm_reduce_ws, sk, X, A, out, (FAKE + 16, need)) == sm.SM_ERR_ALIGN
+    assert _err(sm.sm_local_gemm_reduce_ws, sk, X, A, out, ws, 7) == sm.SM_ERR_ARG
+    assert _err(sm.sm_local_gemm_reduce_ws, sk, X, A, _fb(8192, elems=15 * 8192), ws) == sm.SM_ERR_SHAPE
+    assert _err(sm.sm_local_gemm_reduce_ws, sk, X, _fb(8192, 3584 * 8192, dt=BF), out, ws) == sm.SM_ERR_ARG
+    odd = sm.sm_plan({"T": 3}, "P(None, 'T')", "P('T', None)", 16, 96, 64)
+    assert _err(sm.sm_local_gemm_reduce_ws, odd, _fb(96, dt=BF), _fb(64, dt=BF), _fb(64), (FAKE, 1 << 30),
+                sm.SM_REDUCESCATTER) == sm.SM_ERR_INDIVISIBLE
+    many = sm.sm_plan({"T": 128}, "P(None, 'T')", "P('T', None)", 16, 128 * 16, 64)
+    assert _err(sm.sm_local_gemm_reduce_ws, many, _fb(2048, dt=BF), _fb(64, dt=BF), _fb(64), (FAKE, 1 << 30)) \
+        == sm.SM_ERR_SHAPE  # more than 64 partials per group
+    # a valid call passes every argument check and reaches the device-memory
+    # check, which refuses the fake pointers (or finds no device at all)
+    assert _err(sm.sm_local_gemm_reduce_ws, sk, X, A, out, ws) in (sm.SM_ERR_ARG, sm.SM_ERR_HIP)
+    assert "A: " in sm.sm_last_error()
+
+
 def test_reduce_and_gather_validation():
     p3 = sm.sm_plan({"X": 2, "Y": 2}, "P('X', 'Y')", "P('Y', None)", 12, 16, 8)
     p1 = sm.sm_plan({"X": 2}, "P('X', None)", "P()", 8, 8, 8)

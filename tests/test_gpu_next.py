@@ -9,7 +9,8 @@ import local_shard_gemm_amd as sm
 import workloads as wl
 from oracle import planner, reference as ref
 
-from hip_cases import DEV, REL_TOL, f32_bits_equal, guard_intact, guarded, run_partials, sample_rows, say, to_dev
+from hip_cases import (DEV, FREIVALDS_FLOAT_TOL, REL_TOL, f32_bits_equal, guard_intact, guarded, run_partials,
+                       sample_rows, say, to_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -164,6 +165,9 @@ def test_fused_reduce_full_downproj():
             err = ref.rel_frobenius(fused[rows].cpu().numpy(), want)
             say("fused float rel err", err)
             assert err <= REL_TOL
+            fr = ref.freivalds(A, (0, 0, I, J), B, (0, 0, J, K), fused.cpu().numpy(), trials=1, ints=False)
+            say("fused whole-output Freivalds residual", fr)
+            assert fr <= FREIVALDS_FLOAT_TOL
         del Ad, Bd, fused
 
 
@@ -252,14 +256,14 @@ def test_sp_tail_full_mlp_with_affine():
     out = torch.empty(B_, D, device=DEV)
     sm.sm_reduce_scatter_layernorm(p2, sm.buf(P), sm.buf(out), torch.from_numpy(gamma).to(DEV),
                                    torch.from_numpy(beta).to(DEV), 1e-5)
-    # oracle: the partials from the GPU's own H (H itself is checked against
-    # the oracle in the MLP tests), summed in rank order, then layer norm
-    Hn = H.cpu()
+    # oracle only: the chain's rank-ordered Z rows from the oracle's own H,
+    # then the layer norm of each owned row
+    q1 = planner.plan(dict(w.mesh), w.operand("X").spec, w.operand("W1").spec, B_, D, F)
     m = q2.c_local[0] // q2.n_partials
     for y in range(q2.n_partials):
         rows = [y * m + r for r in sample_rows(m, 3, 820 + y)]
-        parts = [ref.unit_partial(q2, Hn, W2, u, rows=rows) for u in range(q2.n_units)]
-        want = ref.layer_norm(ref.sum_ranked(parts), gamma, beta, 1e-5)
+        _, z = ref.mlp_chain(q1, q2, X, W1, W2, rows=rows)
+        want = ref.layer_norm(z, gamma, beta, 1e-5)
         got = out[rows].cpu().numpy()
         assert ref.rel_frobenius(got, want) <= LN_TOL, y
 
