@@ -23,8 +23,9 @@
  *  - All argument checks run on the host before anything is enqueued, so a
  *    non-OK status other than SM_ERR_HIP leaves every output untouched.
  *  - Memory: every device buffer is allocated and freed by the caller. The
- *    library allocates no device memory, keeps no device state, starts no
- *    threads. Plans are caller-owned plain structs that need no freeing.
+ *    library allocates no device memory and starts no threads; its only
+ *    device state is the static scratch of sm_local_gemm_reduce_noalloc.
+ *    Plans are caller-owned plain structs that need no freeing.
  *  - Streams: device calls enqueue on the given stream (a hipStream_t
  *    passed as void*; NULL = the null stream) and return without
  *    synchronising. Calls that overlap in time on different streams and
@@ -290,6 +291,24 @@ int32_t sm_local_gemm_reduce_ws(const sm_plan_t* plan, const sm_buf* A, const sm
                                 const sm_buf* out, int32_t mode, int32_t group_begin,
                                 int32_t group_count, void* workspace, int64_t workspace_bytes,
                                 void* stream);
+
+/* sm_local_gemm_reduce_ws without a workspace argument, for callers that
+ * cannot allocate device memory: code under stream capture, tight serving
+ * loops, harnesses that forbid allocation. The call allocates nothing (no
+ * hipMalloc, hipFree or allocating library routine). Skinny products keep
+ * their counters and partials in the library's static device array
+ * (64 KiB of counters + 16 MiB of partials, held by every GPU the library
+ * runs on until the process ends); a call that needs more is refused with
+ * SM_ERR_SHAPE before anything is launched (use sm_local_gemm_reduce_ws).
+ * The first call on a device also enqueues, on `stream`, the clearing of
+ * that device's counters; every completed call leaves them zero. All calls
+ * on one GPU share the array: calls that overlap in time (other streams
+ * without synchronisation, other threads) race. Products of more than 64
+ * rows need no scratch and run as sm_local_gemm_reduce. Results are bit for
+ * bit those of sm_local_gemm_reduce_ws. Errors as sm_local_gemm_reduce_ws. */
+int32_t sm_local_gemm_reduce_noalloc(const sm_plan_t* plan, const sm_buf* A, const sm_buf* B,
+                                     const sm_buf* out, int32_t mode, int32_t group_begin,
+                                     int32_t group_count, void* stream);
 
 /* Sequence-parallel tail (ana-alekseeva.com "Sequence parallelism": the
  * all-reduce of a tensor-parallel block becomes a reduce-scatter, layer norm

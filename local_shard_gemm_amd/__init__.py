@@ -55,7 +55,7 @@ EXPORTED = (
     "sm_abi_version", "sm_plan_size", "sm_status_str", "sm_last_error", "sm_mesh_init",
     "sm_parse_spec", "sm_plan", "sm_rank_info", "sm_local_gemm", "sm_reduce_partials",
     "sm_gather_shards", "sm_plan_gathered", "sm_local_gemm_reduce", "sm_reduce_scatter_layernorm",
-    "sm_reshard", "sm_gemm_reduce_workspace", "sm_local_gemm_reduce_ws",
+    "sm_reshard", "sm_gemm_reduce_workspace", "sm_local_gemm_reduce_ws", "sm_local_gemm_reduce_noalloc",
 )
 
 
@@ -161,6 +161,9 @@ def load(path: str = LIB_PATH):
         lib.sm_local_gemm_reduce_ws.restype = i32
         lib.sm_local_gemm_reduce_ws.argtypes = [P(sm_plan_t), P(sm_buf), P(sm_buf), P(sm_buf), i32, i32, i32, vp, i64,
                                                 vp]
+        lib.sm_local_gemm_reduce_noalloc.restype = i32
+        lib.sm_local_gemm_reduce_noalloc.argtypes = [P(sm_plan_t), P(sm_buf), P(sm_buf), P(sm_buf), i32, i32, i32,
+                                                     vp]
         lib.sm_reduce_scatter_layernorm.restype = i32
         lib.sm_reduce_scatter_layernorm.argtypes = [P(sm_plan_t), P(sm_buf), P(sm_buf), vp, vp, ctypes.c_float,
                                                     i32, i32, vp]
@@ -325,6 +328,17 @@ def sm_local_gemm_reduce_ws(plan: sm_plan_t, A, B, out, workspace, mode: int = S
         wp, wn = ctypes.c_void_p(workspace.data_ptr()), workspace.numel() * workspace.element_size()
     _check(load().sm_local_gemm_reduce_ws(ctypes.byref(plan), ctypes.byref(a), ctypes.byref(b), ctypes.byref(o),
                                           mode, group_begin, group_count, wp, wn, _stream(stream)))
+
+
+def sm_local_gemm_reduce_noalloc(plan: sm_plan_t, A, B, out, mode: int = SM_ALLREDUCE, group_begin: int = 0,
+                                 group_count: Optional[int] = None, stream=None) -> None:
+    """sm_local_gemm_reduce_ws on the library's static scratch: no workspace
+    argument and no device allocation."""
+    if group_count is None:
+        group_count = plan.n_groups - group_begin
+    a, b, o = _as_buf(A), _as_buf(B), _as_buf(out)
+    _check(load().sm_local_gemm_reduce_noalloc(ctypes.byref(plan), ctypes.byref(a), ctypes.byref(b),
+                                               ctypes.byref(o), mode, group_begin, group_count, _stream(stream)))
 
 
 def sm_reduce_scatter_layernorm(plan: sm_plan_t, partials, out, gamma=None, beta=None, eps: float = 1e-5,

@@ -12,9 +12,6 @@
 #include "internal.h"
 #include "kernels.h"
 
-namespace shardmm {
-ReduceWorkspace reduce_workspace(const sm_plan_t& p, int64_t groups);
-}  // namespace shardmm
 
 namespace shardmm {
 
@@ -426,14 +423,16 @@ ReduceWorkspace reduce_workspace(const sm_plan_t& p, int64_t groups) {
 }
 
 // Local products of a case-3 plan and their rank-ordered reduction, for
-// sm_local_gemm_reduce (ws == nullptr), sm_local_gemm_reduce_ws and the
-// no-allocation entry point. Products of more than 64 rows: one tile-kernel
-// launch per batch of groups, K = the group's whole J, no workspace.
-// Skinny products: the split-J kernel with the fused reduction, whose
-// counters and partials live in `ws` (ws_bytes long).
+// sm_local_gemm_reduce (no scratch), sm_local_gemm_reduce_ws (the caller's
+// workspace) and the no-allocation entry point (the library's static
+// scratch). Products of more than 64 rows: one tile-kernel launch per batch
+// of groups, K = the group's whole J, no scratch. Skinny products: the
+// split-J kernel with the fused reduction, whose counters and partials live
+// in the scratch `sc` describes.
 int32_t gemm_reduce_impl(const sm_plan_t* plan, const sm_buf* A, const sm_buf* B, const sm_buf* out, int32_t mode,
-                         int32_t group_begin, int32_t group_count, void* ws, int64_t ws_bytes, hipStream_t s,
+                         int32_t group_begin, int32_t group_count, const ReduceScratch& sc, void* stream,
                          const char* where) {
+  hipStream_t s = static_cast<hipStream_t>(stream);
   int32_t st = check_plan(plan);
   if (st) return st;
   const sm_plan_t& p = *plan;
@@ -454,7 +453,7 @@ int32_t gemm_reduce_impl(const sm_plan_t* plan, const sm_buf* A, const sm_buf* B
   const int64_t m = p.c_local[0], n = p.c_local[1], kfull = p.J;
   const int32_t N = p.n_partials;
   const bool skinny = m <= kSkinnyMaxM;
-  if (skinny && !ws)
+  if (skinny && sc.kind == ReduceScratch::kNone)
     return fail(SM_ERR_SHAPE, "local products of at most 64 rows reduce through a workspace "
                               "(sm_local_gemm_reduce_ws)");
   if (m > INT32_MAX / 2 || n > INT32_MAX / 2 || kfull > INT32_MAX / 2) return fail(SM_ERR_SHAPE, "shape too large");
@@ -471,12 +470,27 @@ int32_t gemm_reduce_impl(const sm_plan_t* plan, const sm_buf* A, const sm_buf* B
     return st;
   }
   ReduceWorkspace W{};
+  uint32_t* counters = nullptr;
+  float* parts = nullptr;
   if (skinny) {
     W = reduce_workspace(p, group_count);
-    if (reinterpret_cast<uintptr_t>(ws) % 256) return fail(SM_ERR_ALIGN, "workspace not 256-byte aligned");
-    if (ws_bytes < W.counter_bytes + W.part_bytes)
-      return fail(SM_ERR_SHAPE, "workspace of " + std::to_string(ws_bytes) + " bytes, the call needs " +
-                                    std::to_string(W.counter_bytes + W.part_bytes));
+    if (sc.kind == ReduceScratch::kCaller) {
+      if (!sc.ws) return fail(SM_ERR_ARG, "NULL workspace");
+      if (reinterpret_cast<uintptr_t>(sc.ws) % 256) return fail(SM_ERR_ALIGN, "workspace not 256-byte aligned");
+      if (sc.ws_bytes < W.counter_bytes + W.part_bytes)
+        return fail(SM_ERR_SHAPE, "workspace of " + std::to_string(sc.ws_bytes) + " bytes, the call needs " +
+                                      std::to_string(W.counter_bytes + W.part_bytes));
+      counters = static_cast<uint32_t*>(sc.ws);
+      parts = reinterpret_cast<float*>(static_cast<char*>(sc.ws) + W.counter_bytes);
+    } else if (sc.kind == ReduceScratch::kFixed) {
+      if (W.counter_bytes > sc.counter_cap || W.part_bytes > sc.part_cap)
+        return fail(SM_ERR_SHAPE, "the call needs " + std::to_string(W.counter_bytes) + " bytes of counters and " +
+                                      std::to_string(W.part_bytes) + " bytes of partials; the static scratch holds " +
+                                      std::to_string(sc.counter_cap) + " and " + std::to_string(sc.part_cap) +
+                                      " (use sm_local_gemm_reduce_ws)");
+      counters = sc.counters;
+      parts = sc.parts;
+    }
   }
 
   GemmLaunch L;
@@ -563,11 +577,10 @@ int32_t gemm_reduce_impl(const sm_plan_t* plan, const sm_buf* A, const sm_buf* B
   if ((st = check_device_memory(A->ptr, "A")) || (st = check_device_memory(B->ptr, "B")) ||
       (st = check_device_memory(out->ptr, "out")))
     return st;
-  if (skinny && (st = check_device_memory(ws, "workspace"))) return st;
+  if (skinny && sc.kind == ReduceScratch::kCaller && (st = check_device_memory(sc.ws, "workspace"))) return st;
+  if (sc.kind == ReduceScratch::kValidate) return SM_OK;
 
   if (skinny) {
-    uint32_t* counters = static_cast<uint32_t*>(ws);
-    float* parts = reinterpret_cast<float*>(static_cast<char*>(ws) + W.counter_bytes);
     SkinnyReduce R;
     std::memset(&R, 0, sizeof R);
     R.part_stride = m * W.ldp;
@@ -610,8 +623,8 @@ int32_t gemm_reduce_impl(const sm_plan_t* plan, const sm_buf* A, const sm_buf* B
 extern "C" int32_t sm_local_gemm_reduce(const sm_plan_t* plan, const sm_buf* A, const sm_buf* B, const sm_buf* out,
                                         int32_t mode, int32_t group_begin, int32_t group_count, void* stream) {
   clear_error();
-  return gemm_reduce_impl(plan, A, B, out, mode, group_begin, group_count, nullptr, 0,
-                          static_cast<hipStream_t>(stream), "sm_local_gemm_reduce launch");
+  return gemm_reduce_impl(plan, A, B, out, mode, group_begin, group_count, ReduceScratch{}, stream,
+                          "sm_local_gemm_reduce launch");
 }
 
 extern "C" int32_t sm_gemm_reduce_workspace(const sm_plan_t* plan, int32_t group_count, int64_t* bytes) {
@@ -631,7 +644,10 @@ extern "C" int32_t sm_local_gemm_reduce_ws(const sm_plan_t* plan, const sm_buf* 
                                            int32_t group_count, void* workspace, int64_t workspace_bytes,
                                            void* stream) {
   clear_error();
-  if (plan && plan->c_local[0] <= kSkinnyMaxM && !workspace) return fail(SM_ERR_ARG, "NULL workspace");
-  return gemm_reduce_impl(plan, A, B, out, mode, group_begin, group_count, workspace, workspace_bytes,
-                          static_cast<hipStream_t>(stream), "sm_local_gemm_reduce_ws launch");
+  ReduceScratch sc;
+  sc.kind = ReduceScratch::kCaller;
+  sc.ws = workspace;
+  sc.ws_bytes = workspace_bytes;
+  return gemm_reduce_impl(plan, A, B, out, mode, group_begin, group_count, sc, stream,
+                          "sm_local_gemm_reduce_ws launch");
 }

@@ -56,4 +56,31 @@ int32_t check_device_memory(const void* ptr, const char* what);
 // Stacked blocks of rows x cols do not overlap.
 int32_t check_stacked(const sm_buf* b, int64_t rows, int64_t cols, const char* what);
 
+// ---- the fused local products + reduction (case 3)
+
+struct ReduceWorkspace;
+// Workspace layout of a fused skinny reduction over `groups` groups.
+ReduceWorkspace reduce_workspace(const sm_plan_t& p, int64_t groups);
+// Where a fused skinny reduction keeps its counters and partials.
+struct ReduceScratch {
+  enum Kind : int32_t {
+    kNone = 0,      // none (sm_local_gemm_reduce): skinny products are refused
+    kCaller = 1,    // the caller's workspace `ws`, split as documented for sm_local_gemm_reduce_ws
+    kFixed = 2,     // fixed regions (the static scratch): counters, then partials, each with a capacity
+    kValidate = 3,  // run every host check, launch nothing
+  };
+  int32_t kind = kNone;
+  void* ws = nullptr;
+  int64_t ws_bytes = 0;
+  uint32_t* counters = nullptr;
+  int64_t counter_cap = 0;
+  float* parts = nullptr;
+  int64_t part_cap = 0;
+};
+// sm_local_gemm_reduce and its scratch variants: every check on the host,
+// then the launches on `stream` (a hipStream_t).
+int32_t gemm_reduce_impl(const sm_plan_t* plan, const sm_buf* A, const sm_buf* B, const sm_buf* out, int32_t mode,
+                         int32_t group_begin, int32_t group_count, const ReduceScratch& sc, void* stream,
+                         const char* where);
+
 }  // namespace shardmm
