@@ -159,6 +159,11 @@ typedef struct {
 int32_t sm_abi_version(void);
 size_t sm_plan_size(void);
 
+/* sha256 (64 hex digits) of the sources this library was built from, for
+ * bindings to refuse a build older than its sources ("unknown" when the
+ * build did not stamp one). */
+const char* sm_build_digest(void);
+
 /* Human-readable name of a status; thread-local detail of the last error. */
 const char* sm_status_str(int32_t status);
 const char* sm_last_error(void);
@@ -184,7 +189,15 @@ int32_t sm_plan(const sm_mesh* mesh, const sm_spec* a, const sm_spec* b,
                 int64_t I, int64_t J, int64_t K, int32_t in_dtype,
                 int32_t out_dtype, sm_plan_t* out);
 
-/* Where rank `rank` sits in the plan. */
+/* Where rank `rank` sits in the plan: its mesh coordinates, the unit it
+ * computes (group g and partial index y), the blocks of A, B and C it holds
+ * with their global coordinates, and, for case 3, the rows it owns after a
+ * reduce-scatter. This is the per-rank side of the output interface:
+ * finished values are handed over together with each rank's coordinates
+ * (semiaifoundry.com "Sharded matrix multiplication and result ownership",
+ * section "Specifications and interfaces", Interfaces table), and every
+ * block of an operand names the devices that hold it (learntpu.dev ch05,
+ * sharding sandbox). Errors: SM_ERR_ARG for a rank outside [0, n_ranks). */
 int32_t sm_rank_info(const sm_plan_t* plan, int32_t rank, sm_rank_info_t* out);
 
 /* Cases 2 and 4 by composition (lingze.zone "Case 2" and "Case 4": all-gather

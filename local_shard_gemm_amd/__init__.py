@@ -52,7 +52,7 @@ SM_EPI_STORE, SM_EPI_GELU_TANH = 0, 1
 SM_WHAT_A, SM_WHAT_B, SM_WHAT_C_BLOCKS, SM_WHAT_C_SCATTERED, SM_WHAT_C_PARTIAL = 0, 1, 2, 3, 4
 
 EXPORTED = (
-    "sm_abi_version", "sm_plan_size", "sm_status_str", "sm_last_error", "sm_mesh_init",
+    "sm_abi_version", "sm_plan_size", "sm_build_digest", "sm_status_str", "sm_last_error", "sm_mesh_init",
     "sm_parse_spec", "sm_plan", "sm_rank_info", "sm_local_gemm", "sm_reduce_partials",
     "sm_gather_shards", "sm_plan_gathered", "sm_local_gemm_reduce", "sm_reduce_scatter_layernorm",
     "sm_reshard", "sm_gemm_reduce_workspace", "sm_local_gemm_reduce_ws", "sm_local_gemm_reduce_noalloc",
@@ -114,26 +114,51 @@ class ShardmmError(RuntimeError):
 
 
 _lib = None
+_lib_path = None
 _lock = threading.Lock()
 
 
-def load(path: str = LIB_PATH):
-    """Load libshardmm.so (building it first only if it does not exist)."""
-    global _lib
+def ensure_fresh(path: str = LIB_PATH) -> None:
+    """Build the in-tree library when it is missing or its source stamp
+    differs from the current sources; raise if that is needed and cannot be
+    done (no hipcc), so that a stale build is never loaded."""
+    from . import build as _build
+
+    want = _build.source_digest()
+    have = _build.library_digest(path)
+    if have == want:
+        return
+    try:
+        _build.build()
+    except Exception as e:  # noqa: BLE001 - any build failure is reported the same way
+        raise ShardmmError(SM_ERR_ARG, "SM_ERR_ARG",
+                           f"{path} is {'missing' if have is None else 'older than its sources'} and could not be "
+                           f"rebuilt: {e}") from e
+    if _build.library_digest(path) != want:
+        raise ShardmmError(SM_ERR_ARG, "SM_ERR_ARG", f"{path}: the rebuilt library carries another source stamp")
+
+
+def load(path: Optional[str] = None):
+    """Load libshardmm. The default is the in-tree libshardmm.so, rebuilt
+    first if it is missing or older than its sources; the environment
+    variable SHARDMM_LIB names another build to load instead (as is; a
+    build of the host planner alone binds only the host calls)."""
+    global _lib, _lib_path
     with _lock:
         if _lib is not None:
             return _lib
-        if not os.path.exists(path):
-            from . import build as _build
-
-            _build.build()
+        path = path or os.environ.get("SHARDMM_LIB") or LIB_PATH
+        if os.path.abspath(path) == os.path.abspath(LIB_PATH):
+            ensure_fresh(path)
         lib = ctypes.CDLL(path)
         P = ctypes.POINTER
-        i32, i64, vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p
+        i32, i64 = ctypes.c_int32, ctypes.c_int64
         lib.sm_abi_version.restype = i32
         lib.sm_abi_version.argtypes = []
         lib.sm_plan_size.restype = ctypes.c_size_t
         lib.sm_plan_size.argtypes = []
+        lib.sm_build_digest.restype = ctypes.c_char_p
+        lib.sm_build_digest.argtypes = []
         lib.sm_status_str.restype = ctypes.c_char_p
         lib.sm_status_str.argtypes = [i32]
         lib.sm_last_error.restype = ctypes.c_char_p
@@ -146,35 +171,42 @@ def load(path: str = LIB_PATH):
         lib.sm_plan.argtypes = [P(sm_mesh), P(sm_spec), P(sm_spec), i64, i64, i64, i32, i32, P(sm_plan_t)]
         lib.sm_rank_info.restype = i32
         lib.sm_rank_info.argtypes = [P(sm_plan_t), i32, P(sm_rank_info_t)]
-        lib.sm_local_gemm.restype = i32
-        lib.sm_local_gemm.argtypes = [P(sm_plan_t), P(sm_buf), P(sm_buf), P(sm_buf), i32, i32, i32, vp]
-        lib.sm_reduce_partials.restype = i32
-        lib.sm_reduce_partials.argtypes = [P(sm_plan_t), P(sm_buf), P(sm_buf), i32, i32, i32, vp]
-        lib.sm_gather_shards.restype = i32
-        lib.sm_gather_shards.argtypes = [P(sm_plan_t), i32, P(sm_buf), P(sm_buf), vp]
         lib.sm_plan_gathered.restype = i32
         lib.sm_plan_gathered.argtypes = [P(sm_plan_t), P(sm_plan_t)]
-        lib.sm_local_gemm_reduce.restype = i32
-        lib.sm_local_gemm_reduce.argtypes = [P(sm_plan_t), P(sm_buf), P(sm_buf), P(sm_buf), i32, i32, i32, vp]
-        lib.sm_gemm_reduce_workspace.restype = i32
-        lib.sm_gemm_reduce_workspace.argtypes = [P(sm_plan_t), i32, P(i64)]
-        lib.sm_local_gemm_reduce_ws.restype = i32
-        lib.sm_local_gemm_reduce_ws.argtypes = [P(sm_plan_t), P(sm_buf), P(sm_buf), P(sm_buf), i32, i32, i32, vp, i64,
-                                                vp]
-        lib.sm_local_gemm_reduce_noalloc.restype = i32
-        lib.sm_local_gemm_reduce_noalloc.argtypes = [P(sm_plan_t), P(sm_buf), P(sm_buf), P(sm_buf), i32, i32, i32,
-                                                     vp]
-        lib.sm_reduce_scatter_layernorm.restype = i32
-        lib.sm_reduce_scatter_layernorm.argtypes = [P(sm_plan_t), P(sm_buf), P(sm_buf), vp, vp, ctypes.c_float,
-                                                    i32, i32, vp]
-        lib.sm_reshard.restype = i32
-        lib.sm_reshard.argtypes = [P(sm_mesh), P(sm_spec), P(sm_spec), i64, i64, i32, P(sm_buf), P(sm_buf), vp]
+        if hasattr(lib, "sm_local_gemm"):
+            _bind_device_calls(lib)
         if lib.sm_abi_version() != SM_ABI_VERSION:
             raise ShardmmError(SM_ERR_ARG, "SM_ERR_ARG", "libshardmm ABI version mismatch")
         if lib.sm_plan_size() != ctypes.sizeof(sm_plan_t):
             raise ShardmmError(SM_ERR_ARG, "SM_ERR_ARG", "sm_plan_t layout mismatch")
-        _lib = lib
+        _lib, _lib_path = lib, path
         return lib
+
+
+def _bind_device_calls(lib) -> None:
+    P = ctypes.POINTER
+    i32, i64, vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p
+    lib.sm_local_gemm.restype = i32
+    lib.sm_local_gemm.argtypes = [P(sm_plan_t), P(sm_buf), P(sm_buf), P(sm_buf), i32, i32, i32, vp]
+    lib.sm_reduce_partials.restype = i32
+    lib.sm_reduce_partials.argtypes = [P(sm_plan_t), P(sm_buf), P(sm_buf), i32, i32, i32, vp]
+    lib.sm_gather_shards.restype = i32
+    lib.sm_gather_shards.argtypes = [P(sm_plan_t), i32, P(sm_buf), P(sm_buf), vp]
+    lib.sm_local_gemm_reduce.restype = i32
+    lib.sm_local_gemm_reduce.argtypes = [P(sm_plan_t), P(sm_buf), P(sm_buf), P(sm_buf), i32, i32, i32, vp]
+    lib.sm_gemm_reduce_workspace.restype = i32
+    lib.sm_gemm_reduce_workspace.argtypes = [P(sm_plan_t), i32, P(i64)]
+    lib.sm_local_gemm_reduce_ws.restype = i32
+    lib.sm_local_gemm_reduce_ws.argtypes = [P(sm_plan_t), P(sm_buf), P(sm_buf), P(sm_buf), i32, i32, i32, vp, i64,
+                                            vp]
+    lib.sm_local_gemm_reduce_noalloc.restype = i32
+    lib.sm_local_gemm_reduce_noalloc.argtypes = [P(sm_plan_t), P(sm_buf), P(sm_buf), P(sm_buf), i32, i32, i32,
+                                                 vp]
+    lib.sm_reduce_scatter_layernorm.restype = i32
+    lib.sm_reduce_scatter_layernorm.argtypes = [P(sm_plan_t), P(sm_buf), P(sm_buf), vp, vp, ctypes.c_float,
+                                                i32, i32, vp]
+    lib.sm_reshard.restype = i32
+    lib.sm_reshard.argtypes = [P(sm_mesh), P(sm_spec), P(sm_spec), i64, i64, i32, P(sm_buf), P(sm_buf), vp]
 
 
 def _check(status: int) -> None:
@@ -373,4 +405,4 @@ def sm_gather_shards(plan: sm_plan_t, what: int, shards, out, stream=None) -> No
 
 def loaded_library_path() -> str:
     load()
-    return LIB_PATH
+    return _lib_path

@@ -2,7 +2,9 @@
 
 Every source under csrc/ is compiled for gfx950 only, with packed-fp32
 instruction generation disabled, and linked into
-``local_shard_gemm_amd/libshardmm.so`` next to this file.
+``local_shard_gemm_amd/libshardmm.so`` next to this file. The library is
+stamped with a sha256 of its sources (``source_digest``), which the binding
+compares before loading it, so a stale build is never used.
 """
 from __future__ import annotations
 
@@ -45,9 +47,52 @@ def sources():
     return sorted(glob.glob(os.path.join(CSRC, "*.cpp")) + glob.glob(os.path.join(CSRC, "*.hip")))
 
 
-def _compile(src: str, verbose: bool) -> str:
+DIGEST_MARKER = b"SM_SOURCE_DIGEST="
+
+
+def digest_inputs(root: str = ROOT):
+    """Files whose contents decide the built library: every source and
+    header under csrc/, the public header, and this build script (flags)."""
+    pkg = os.path.join(root, "local_shard_gemm_amd")
+    files = []
+    for pat in ("*.cpp", "*.hip", "*.h"):
+        files += glob.glob(os.path.join(pkg, "csrc", pat))
+    files.append(os.path.join(root, "include", "shardmm.h"))
+    files.append(os.path.join(pkg, "build.py"))
+    return sorted(files, key=lambda f: os.path.relpath(f, root))
+
+
+def source_digest(root: str = ROOT) -> str:
+    """sha256 over (relative path, contents) of digest_inputs(root)."""
+    import hashlib
+
+    h = hashlib.sha256()
+    for f in digest_inputs(root):
+        h.update(os.path.relpath(f, root).encode() + b"\0")
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+        h.update(b"\0")
+    return h.hexdigest()
+
+
+def library_digest(path: str = None):
+    """The source digest stamped into a built library (None if absent)."""
+    path = path or LIB
+    try:
+        with open(path, "rb") as f:
+            data = f.read()
+    except OSError:
+        return None
+    i = data.find(DIGEST_MARKER)
+    if i < 0:
+        return None
+    d = data[i + len(DIGEST_MARKER):i + len(DIGEST_MARKER) + 64]
+    return d.decode("ascii", "replace") if len(d) == 64 else None
+
+
+def _compile(src: str, verbose: bool, digest: str) -> str:
     obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
-    cmd = [hipcc(), *COMMON, "-c", src, "-o", obj]
+    cmd = [hipcc(), *COMMON, f'-DSM_SOURCE_DIGEST="{digest}"', "-c", src, "-o", obj]
     if src.endswith(".cpp"):
         cmd[1:1] = ["-x", "hip"]
     if verbose:
@@ -65,8 +110,9 @@ def _compile(src: str, verbose: bool) -> str:
 def build(verbose: bool = False, jobs: int = 8) -> str:
     os.makedirs(BUILD_DIR, exist_ok=True)
     srcs = sources()
+    digest = source_digest()
     with ThreadPoolExecutor(max_workers=max(1, min(jobs, len(srcs)))) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), srcs))
+        objs = list(ex.map(lambda s: _compile(s, verbose, digest), srcs))
     tmp = LIB + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     if verbose:

@@ -14,7 +14,15 @@
 
 #include "internal.h"
 
+#ifndef SM_SOURCE_DIGEST
+#define SM_SOURCE_DIGEST "unknown"
+#endif
+
 namespace shardmm {
+
+// The build's source digest behind a fixed marker, so that the binding can
+// read it from the file before loading the library.
+static const char kBuildDigest[] = "SM_SOURCE_DIGEST=" SM_SOURCE_DIGEST;
 
 static thread_local std::string g_last_error;
 
@@ -392,7 +400,7 @@ int32_t sm_plan(const sm_mesh* mesh, const sm_spec* a, const sm_spec* b, int64_t
     // Case 4: a shared axis on the non-contracting dims; only diagonal blocks
     // are formed. Fix by gathering the smaller operand over the shared axes.
     p.kase = SM_CASE4;
-    p.gather_operand = (I * J <= J * K) ? 0 : 1;
+    p.gather_operand = I <= K ? 0 : 1;  // bytes I*J vs J*K (J >= 1), without the product
     p.gather_axes = a_i & b_k;
   } else if (a->n[1] > 0 && b->n[0] > 0) {
     bool same = a->n[1] == b->n[0];
@@ -501,3 +509,5 @@ int32_t sm_rank_info(const sm_plan_t* plan, int32_t rank, sm_rank_info_t* out) {
 int32_t shardmm::validate_spec(const sm_mesh& mesh, const sm_spec& s, const char* what) {
   return validate_spec_impl(mesh, s, what);
 }
+
+extern "C" const char* sm_build_digest(void) { return shardmm::kBuildDigest + sizeof("SM_SOURCE_DIGEST=") - 1; }

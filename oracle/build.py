@@ -31,13 +31,16 @@ def build(verbose: bool = False) -> str:
 
 
 def load_library():
+    """liboracle.so (built on first use), or the build ORACLE_LIB names
+    (the tests' sanitizer run loads an instrumented build that way)."""
     global _lib
     with _lock:
         if _lib is not None:
             return _lib
-        if not os.path.exists(LIB):
+        path = os.environ.get("ORACLE_LIB") or LIB
+        if path == LIB and not os.path.exists(LIB):
             build()
-        lib = ctypes.CDLL(LIB)
+        lib = ctypes.CDLL(path)
         i64, vp, dp = ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p
         lib.orc_num_threads.restype = ctypes.c_int
         lib.orc_matmul.argtypes = [vp, ctypes.c_int, i64, vp, ctypes.c_int, i64, dp, i64,

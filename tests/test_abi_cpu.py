@@ -199,6 +199,19 @@ def test_planner_brute_force_against_reference(mesh_axes):
     _compare(mesh_axes, specs[1], specs[1], *shapes[2])
 
 
+@pytest.mark.parametrize("I,J,K", [(1 << 40, 1 << 40, 1 << 39), (1 << 39, 1 << 40, 1 << 40),
+                                   (1 << 40, 1 << 40, 1 << 40), (2, 1 << 40, 4)])
+def test_case4_extreme_shapes_match_reference(I, J, K):
+    """Case 4 gathers the smaller input by bytes (I*J against J*K); at the
+    largest accepted dimensions (2^40) those products reach 2^80, and the
+    library's choice must still be the oracle planner's (exact integers)."""
+    for mesh_axes, a, b in (([("X", 2)], ("X",), ("X",)), ([("X", 2), ("Y", 4)], ("XY",), ("XY",))):
+        names = [n for n, _ in mesh_axes]
+        sa = (tuple(a[0]), ())
+        sb = ((), tuple(b[0]))
+        _compare(mesh_axes, sa, sb, I, J, K)
+
+
 def test_sandbox_default_through_the_library():
     p = sm.sm_plan({"X": 4, "Y": 2}, "P('X', 'Y')", "P('Y', None)", 8192, 28672, 8192)
     assert p.kase == sm.SM_CASE3 and tuple(p.a_local) == (2048, 14336) and p.a_copies == 1
