@@ -137,7 +137,24 @@ def rate(bound: str, work: float, ms: float, cold_ms=None) -> dict:
     return out
 
 
-def measure_rows(back_to_back, cold, stream) -> dict:
+def oracle_sample(entry: dict, fn, work: float, what: str) -> None:
+    """Attach to a roofline entry the oracle's rate on a bounded sample of
+    the same operation: fn() runs the oracle (fp64, the host's cores) on the
+    sample and `work` is that sample's algorithmic flops or bytes, counted
+    as for the GPU launch, so the two rates compare like for like."""
+    runs, t0 = 0, time.perf_counter()
+    while True:  # repeated until half a second has passed, for a stable rate
+        fn()
+        runs += 1
+        dt = time.perf_counter() - t0
+        if dt >= 0.5:
+            break
+    v = work * runs / dt / (1e12 if entry["unit"] == "TFLOP/s" else 1e9)
+    entry["oracle"] = {"value": float(f"{v:.4g}"), "unit": entry["unit"], "seconds": round(dt / runs, 4),
+                       "runs": runs, "sample": what, "gpu_over_oracle": round(entry["achieved"] / v, 1)}
+
+
+def measure_rows(back_to_back, cold, stream, with_oracle: bool) -> dict:
     """The other rows of the path on their own workloads, each launch timed
     back to back like the step's kernels:
       a4  Megatron MLP chain [4096,4096] . W1[4096,16384] (4 column blocks,
@@ -149,20 +166,26 @@ def measure_rows(back_to_back, cold, stream) -> dict:
           product of the gathered plan;
       f3  the sequence-parallel tail on the MLP's 4 partials: reduce-scatter,
           per-token layer norm (with gamma, beta), all-gather;
-      f4  the all-to-all reshard A[I,J_X] -> A[I_X,J] of a bf16 [4096,4096]."""
+      f4  the all-to-all reshard A[I,J_X] -> A[I_X,J] of a bf16 [4096,4096];
+      a7  the skinny split-J path with its fused reduce (measure_skinny).
+    With `with_oracle`, every entry also carries the oracle's rate on a
+    bounded sample of the same operation (oracle_sample)."""
+    import numpy as np
     import torch
 
     import local_shard_gemm_amd as sm
     import workloads as wl
 
+    if with_oracle:
+        from oracle import planner, reference as ref
     dev = torch.device("cuda:0")
     rows = {}
+    rng = np.random.default_rng(7)
 
     # a4 (+ f3 on the same partials)
     w = wl.get("mlp")
-    X = wl.make_operand(w.operand("X")).to(dev)
-    W1 = wl.make_operand(w.operand("W1")).to(dev)
-    W2 = wl.make_operand(w.operand("W2")).to(dev)
+    Xc, W1c, W2c = (wl.make_operand(w.operand(n)) for n in ("X", "W1", "W2"))
+    X, W1, W2 = Xc.to(dev), W1c.to(dev), W2c.to(dev)
     B_, D = X.shape
     F = W1.shape[1]
     p1 = sm.sm_plan(dict(w.mesh), w.operand("X").spec, w.operand("W1").spec, B_, D, F, out_dtype=sm.SM_BF16)
@@ -175,14 +198,15 @@ def measure_rows(back_to_back, cold, stream) -> dict:
     l2 = back_to_back(lambda: sm.sm_local_gemm(p2, bh, bw2, bp, sm.SM_EPI_STORE, 0, p2.n_units, stream))
     ar = back_to_back(lambda: sm.sm_reduce_partials(p2, bp, bz, sm.SM_ALLREDUCE, 0, p2.n_groups, stream))
     layer_flops = 2.0 * B_ * D * F
+    red_bytes = (p2.n_partials + 1) * B_ * D * 4.0
     rows["a4_mlp_chain"] = {
         "workload": w.name,
         "layer1_gemm_gelu_bf16": rate("mfma", layer_flops, l1),
         "layer2_gemm": rate("mfma", layer_flops, l2),
-        "allreduce": rate("hbm", (p2.n_partials + 1) * B_ * D * 4.0, ar,
+        "allreduce": rate("hbm", red_bytes, ar,
                           cold(lambda i: (lambda q=(bp if i == 0 else sm.buf(P.clone())):
                                           sm.sm_reduce_partials(p2, q, bz, sm.SM_ALLREDUCE, 0, p2.n_groups, stream)),
-                               (p2.n_partials + 1) * B_ * D * 4.0)),
+                               red_bytes)),
         "chain_ms": round(l1 + l2 + ar, 4),
     }
     g = torch.randn(D, device=dev)
@@ -190,15 +214,38 @@ def measure_rows(back_to_back, cold, stream) -> dict:
     sp = back_to_back(lambda: sm.sm_reduce_scatter_layernorm(p2, bp, bz, g, bta, 1e-5, 0, p2.n_groups, stream))
     sp_cold = cold(lambda i: (lambda q=(bp if i == 0 else sm.buf(P.clone())):
                               sm.sm_reduce_scatter_layernorm(p2, q, bz, g, bta, 1e-5, 0, p2.n_groups, stream)),
-                   (p2.n_partials + 1) * B_ * D * 4.0)
+                   red_bytes)
     rows["f3_sp_tail"] = {"workload": w.name + ": reduce-scatter 4 x [4096,4096] -> layer norm -> all-gather",
-                          **rate("hbm", (p2.n_partials + 1) * B_ * D * 4.0 + 2 * D * 4.0, sp, sp_cold)}
+                          **rate("hbm", red_bytes + 2 * D * 4.0, sp, sp_cold)}
     del X, W1, W2, H, P, Z, bx, bw1, bw2, bh, bp, bz
+    if with_oracle:
+        q1 = planner.plan(dict(w.mesh), w.operand("X").spec, w.operand("W1").spec, B_, D, F)
+        q2 = planner.plan(dict(w.mesh), "P(None, 'T')", w.operand("W2").spec, B_, F, D)
+        R = 256
+        hr = {}
+        oracle_sample(rows["a4_mlp_chain"]["layer1_gemm_gelu_bf16"],
+                      lambda: hr.setdefault("H", ref.mlp_hidden(q1, Xc, W1c, rows=range(R))),
+                      2.0 * R * D * F, f"{R} rows of round_bf16(gelu(X W1_u)), all 4 column blocks")
+        Fk = F // q2.n_partials
+        oracle_sample(rows["a4_mlp_chain"]["layer2_gemm"],
+                      lambda: [ref.view_matmul(hr["H"], (0, u * Fk, R, Fk), W2c, q2.unit_views(u)["B"])
+                               for u in range(q2.n_units)],
+                      2.0 * R * D * F, f"{R} rows of the 4 partials H_u W2_u")
+        R = 1024
+        parts = [rng.standard_normal((R, D)).astype(np.float32).astype(np.float64) for _ in range(q2.n_partials)]
+        gam, bet = np.asarray(g.cpu(), np.float64), np.asarray(bta.cpu(), np.float64)
+        oracle_sample(rows["a4_mlp_chain"]["allreduce"], lambda: ref.sum_ranked(parts),
+                      (q2.n_partials + 1) * R * D * 4.0, f"rank-ordered sum of {q2.n_partials} x [{R},{D}]")
+        oracle_sample(rows["f3_sp_tail"], lambda: ref.layer_norm(ref.sum_ranked(parts), gam, bet, 1e-5),
+                      (q2.n_partials + 1) * R * D * 4.0,
+                      f"rank-ordered sum of {q2.n_partials} x [{R},{D}] then layer norm of each row")
+        del parts, hr
+    del Xc, W1c, W2c
 
     # a6
     w = wl.get("case1")
-    A = wl.make_operand(w.operand("A")).to(dev)
-    Bm = wl.make_operand(w.operand("B")).to(dev)
+    Acpu, Bcpu = wl.make_operand(w.operand("A")), wl.make_operand(w.operand("B"))
+    A, Bm = Acpu.to(dev), Bcpu.to(dev)
     I, J = A.shape
     K = Bm.shape[1]
     p = sm.sm_plan(dict(w.mesh), w.operand("A").spec, w.operand("B").spec, I, J, K)
@@ -213,6 +260,15 @@ def measure_rows(back_to_back, cold, stream) -> dict:
     rows["a6_case1_gather"] = {"workload": w.name,
                                "gemm": rate("mfma", 2.0 * m * n * p.a_local[1] * p.n_units, gm),
                                "gather": rate("hbm", 2 * 4.0 * I * K, ga, ga_cold)}
+    if with_oracle:
+        q = planner.plan(dict(w.mesh), w.operand("A").spec, w.operand("B").spec, I, J, K)
+        R = 512
+        oracle_sample(rows["a6_case1_gather"]["gemm"], lambda: ref.unit_partial(q, Acpu, Bcpu, 0, rows=range(R)),
+                      2.0 * R * n * q.a_local[1], f"{R} rows of unit 0's [{m},{q.a_local[1]}]x[{q.a_local[1]},{n}]")
+        blks = [rng.standard_normal((m, n)) for _ in range(q.n_units)]
+        oracle_sample(rows["a6_case1_gather"]["gather"], lambda: ref.gather(q, blks), 2 * 4.0 * I * K,
+                      f"placing {q.n_units} blocks [{m},{n}] into [{I},{K}]")
+        del blks
 
     # f1: case 2 at the same sizes, A held as 4 column blocks
     mesh = {"X": 4, "Y": 2}
@@ -232,6 +288,18 @@ def measure_rows(back_to_back, cold, stream) -> dict:
         "workload": f"A[I,J_X] . B[J,K] on {{X:4,Y:2}}, I = J = K = {I}",
         "gather_A": rate("hbm", 2 * 2.0 * I * J, gA, gA_cold),
         "gemm": rate("mfma", 2.0 * p_g.c_local[0] * p_g.c_local[1] * p_g.a_local[1] * p_g.n_units, gg)}
+    if with_oracle:
+        qa = planner.plan(mesh, "A[I, J_X]", "B[J, K]", I, J, K)
+        qg = planner.gathered(qa)
+        a_blocks = ref.shard(ref.stored(Acpu)[0], mesh, "A[I, J_X]")
+        oracle_sample(rows["f1_case2_gather_then_gemm"]["gather_A"],
+                      lambda: ref.unshard(a_blocks, mesh, "A[I, J_X]", I, J), 2 * 2.0 * I * J,
+                      f"assembling A [{I},{J}] from its {len(a_blocks)} column blocks")
+        R = 512
+        mg, ng = qg.c_local
+        oracle_sample(rows["f1_case2_gather_then_gemm"]["gemm"],
+                      lambda: ref.unit_partial(qg, Acpu, Bcpu, 0, rows=range(R)), 2.0 * R * ng * qg.a_local[1],
+                      f"{R} rows of unit 0's [{mg},{qg.a_local[1]}]x[{qg.a_local[1]},{ng}]")
 
     # f4: all-to-all reshard of A's column blocks into row blocks
     dst = torch.empty(4, I // 4, J, dtype=torch.bfloat16, device=dev)
@@ -244,11 +312,16 @@ def measure_rows(back_to_back, cold, stream) -> dict:
                               sm.sm_reshard(mesh4, frm, to, I, J, sm.SM_BF16, q, bd4, stream)), 2 * 2.0 * I * J)
     rows["f4_alltoall_reshard"] = {"workload": f"bf16 [{I},{J}] A[I,J_X] -> A[I_X,J] on {{X:4}}",
                                    **rate("hbm", 2 * 2.0 * I * J, rs, rs_cold)}
-    rows["a7_skinny"] = measure_skinny(back_to_back, cold, stream)
+    if with_oracle:
+        src = ref.shard(ref.stored(Acpu)[0], {"X": 4}, "A[I, J_X]")
+        oracle_sample(rows["f4_alltoall_reshard"],
+                      lambda: ref.reshard(src, {"X": 4}, "A[I, J_X]", "A[I_X, J]", I, J), 2 * 2.0 * I * J,
+                      f"the whole all-to-all of [{I},{J}]")
+    rows["a7_skinny"] = measure_skinny(back_to_back, cold, stream, with_oracle)
     return rows
 
 
-def measure_skinny(back_to_back, cold, stream) -> dict:
+def measure_skinny(back_to_back, cold, stream, with_oracle: bool = False) -> dict:
     """Row a7 on the skinny workload (X[16,28672] . A[28672,8192], J split
     over {T:8}): the split-J kernel with the fused rank-ordered all-reduce
     of its 8 partials (sm_local_gemm_reduce_ws), and, for comparison, the
@@ -263,8 +336,8 @@ def measure_skinny(back_to_back, cold, stream) -> dict:
 
     dev = torch.device("cuda:0")
     w = wl.get("skinny")
-    X = wl.make_operand(w.operand("X")).to(dev)
-    A = wl.make_operand(w.operand("A")).to(dev)
+    Xc, Ac = wl.make_operand(w.operand("X")), wl.make_operand(w.operand("A"))
+    X, A = Xc.to(dev), Ac.to(dev)
     B_, J = X.shape
     K = A.shape[1]
     p = sm.sm_plan(dict(w.mesh), w.operand("X").spec, w.operand("A").spec, B_, J, K)
@@ -283,6 +356,12 @@ def measure_skinny(back_to_back, cold, stream) -> dict:
     g = back_to_back(lambda: sm.sm_local_gemm(p, bx, ba, bp, sm.SM_EPI_STORE, 0, p.n_units, stream))
     r = back_to_back(lambda: sm.sm_reduce_partials(p, bp, bo, sm.SM_ALLREDUCE, 0, p.n_groups, stream))
     entry = rate("hbm", work, f, f_cold)
+    if with_oracle:
+        from oracle import planner, reference as ref
+
+        q = planner.plan(dict(w.mesh), w.operand("X").spec, w.operand("A").spec, B_, J, K)
+        oracle_sample(entry, lambda: ref.allreduce(q, ref.partials(q, Xc, Ac)), work,
+                      f"the whole step: {q.n_units} partials X_u A_u and their rank-ordered sum")
     return {"workload": f"{w.name}: X[{B_},{J}] . A[{J},{K}], J split over {{T:{p.n_partials}}}, all-reduce",
             "fused_gemm_reduce": {**entry, "partials_bytes_not_counted": extra},
             "split_j_gemm_then_reduce_ms": round(g + r, 4),
@@ -525,7 +604,7 @@ def main() -> int:
     rows = None
     if not args.no_rows:
         log("bench: the other rows of the path")
-        rows = measure_rows(lambda fn: back_to_back(fn, args.steps), cold, stream)
+        rows = measure_rows(lambda fn: back_to_back(fn, args.steps), cold, stream, not args.no_cpu_baseline)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -577,6 +656,12 @@ def main() -> int:
         "roofline_reduce": {"bound": "hbm", "achieved": round(red_gbps, 1), "peak": PEAK_HBM_GBPS,
                             "unit": "GB/s", "frac": round(red_gbps / PEAK_HBM_GBPS, 4),
                             "traffic": recorded_traffic("reduce", ctx["w"].name)},
+        # the launch the case-3 shard GEMM bar is graded on: one X-group, the
+        # N ranks whose partials are summed together (learntpu.dev ch05,
+        # sharding sandbox "Local matmul", here for both ranks of the group)
+        "roofline_x_group": ({k: subsets["gemm_1_group"][k] for k in
+                              ("bound", "achieved", "peak", "unit", "frac", "avg_ms", "work")}
+                             if subsets and "gemm_1_group" in subsets else None),
         "fused_gemm_reduce": fused,
         "subsets": subsets,
         "rows": rows,

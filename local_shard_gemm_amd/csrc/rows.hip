@@ -12,8 +12,9 @@
 // column chunk of a row, when a launch has few rows) of one job; its 256
 // threads walk it in 16-byte vectors, four vectors per thread
 // per iteration, and issue every partial's loads before the rank-ordered
-// adds so that 4 x N loads per thread are in flight. Loads and stores are
-// non-temporal: nothing is re-read, so the data should not displace L2.
+// adds so that 4 x N loads per thread are in flight. Loads are
+// non-temporal (nothing is re-read, so the data should not displace L2);
+// stores are plain, which the HBM writes back at a higher rate.
 #include "kernels.h"
 
 namespace shardmm {
@@ -50,8 +51,8 @@ __device__ __forceinline__ void st4(float4* p, const float4& v) { *p = v; }
 
 // Rank-ordered sum of NS partials (NS > 0 fixed at compile time, or the
 // runtime count when NS == 0) for one row, float4 path. Sums use
-// non-temporal loads and stores (+40 % over plain ones); a plain copy (NS
-// == 1) measured 5 % faster with plain ones on 8 KiB rows.
+// non-temporal loads (+40 % over plain ones) and plain stores; a plain copy
+// (NS == 1) measured 5 % faster with plain loads on 8 KiB rows.
 template <int NS>
 __device__ __forceinline__ void sum_row_vec(const RowJob& J, int n_sum, int row) {
   constexpr bool kNT = NS != 1;
@@ -93,15 +94,14 @@ __device__ __forceinline__ void sum_row_vec(const RowJob& J, int n_sum, int row)
         }
       }
     }
+    // plain stores for sums and copies alike: on the down-projection's
+    // reduce-scatter (805 MB) they ran at 6.68 TB/s against 6.36 with
+    // non-temporal stores (a lab stream of 2 non-temporal reads + 1 write:
+    // 6.81 vs 6.12 TB/s; a plain write stream alone: 6.97 vs 5.85 TB/s)
 #pragma unroll
     for (int u = 0; u < UNROLL; ++u) {
       const int c4 = base + u * NT;
-      if (c4 < n4) {
-        if (kNT)
-          stnt(reinterpret_cast<float4*>(dst) + c4, acc[u]);
-        else
-          st4(reinterpret_cast<float4*>(dst) + c4, acc[u]);
-      }
+      if (c4 < n4) st4(reinterpret_cast<float4*>(dst) + c4, acc[u]);
     }
   }
 }
