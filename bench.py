@@ -194,8 +194,10 @@ def measure_rows(back_to_back, cold, stream, with_oracle: bool) -> dict:
     P = torch.empty(p2.n_units, B_, D, dtype=torch.float32, device=dev)
     Z = torch.empty(B_, D, dtype=torch.float32, device=dev)
     bx, bw1, bw2, bh, bp, bz = (sm.buf(t) for t in (X, W1, W2, H, P, Z))
-    l1 = back_to_back(lambda: sm.sm_local_gemm(p1, bx, bw1, bh, sm.SM_EPI_GELU_TANH, 0, p1.n_units, stream))
-    l2 = back_to_back(lambda: sm.sm_local_gemm(p2, bh, bw2, bp, sm.SM_EPI_STORE, 0, p2.n_units, stream))
+    l1 = back_to_back(lambda: sm.sm_local_gemm(p1, bx, bw1, bh, sm.SM_EPI_GELU_TANH, 0, p1.n_units, stream),
+                      clock_warm=True)
+    l2 = back_to_back(lambda: sm.sm_local_gemm(p2, bh, bw2, bp, sm.SM_EPI_STORE, 0, p2.n_units, stream),
+                      clock_warm=True)
     ar = back_to_back(lambda: sm.sm_reduce_partials(p2, bp, bz, sm.SM_ALLREDUCE, 0, p2.n_groups, stream))
     layer_flops = 2.0 * B_ * D * F
     red_bytes = (p2.n_partials + 1) * B_ * D * 4.0
@@ -253,7 +255,8 @@ def measure_rows(back_to_back, cold, stream, with_oracle: bool) -> dict:
     Pc = torch.empty(p.n_units, m, n, dtype=torch.float32, device=dev)
     C = torch.empty(I, K, dtype=torch.float32, device=dev)
     ba, bb, bpc, bc = sm.buf(A), sm.buf(Bm), sm.buf(Pc), sm.buf(C)
-    gm = back_to_back(lambda: sm.sm_local_gemm(p, ba, bb, bpc, sm.SM_EPI_STORE, 0, p.n_units, stream))
+    gm = back_to_back(lambda: sm.sm_local_gemm(p, ba, bb, bpc, sm.SM_EPI_STORE, 0, p.n_units, stream),
+                      clock_warm=True)
     ga = back_to_back(lambda: sm.sm_gather_shards(p, sm.SM_WHAT_C_BLOCKS, bpc, bc, stream))
     ga_cold = cold(lambda i: (lambda q=(bpc if i == 0 else sm.buf(Pc.clone())):
                               sm.sm_gather_shards(p, sm.SM_WHAT_C_BLOCKS, q, bc, stream)), 2 * 4.0 * I * K)
@@ -283,7 +286,8 @@ def measure_rows(back_to_back, cold, stream, with_oracle: bool) -> dict:
     gA = back_to_back(lambda: sm.sm_gather_shards(p, sm.SM_WHAT_A, bbl, bag, stream))
     gA_cold = cold(lambda i: (lambda q=(bbl if i == 0 else sm.buf(blocks.clone())):
                               sm.sm_gather_shards(p, sm.SM_WHAT_A, q, bag, stream)), 2 * 2.0 * I * J)
-    gg = back_to_back(lambda: sm.sm_local_gemm(p_g, bag, bb, bcg, sm.SM_EPI_STORE, 0, p_g.n_units, stream))
+    gg = back_to_back(lambda: sm.sm_local_gemm(p_g, bag, bb, bcg, sm.SM_EPI_STORE, 0, p_g.n_units, stream),
+                      clock_warm=True)
     rows["f1_case2_gather_then_gemm"] = {
         "workload": f"A[I,J_X] . B[J,K] on {{X:4,Y:2}}, I = J = K = {I}",
         "gather_A": rate("hbm", 2 * 2.0 * I * J, gA, gA_cold),
@@ -362,10 +366,25 @@ def measure_skinny(back_to_back, cold, stream, with_oracle: bool = False) -> dic
         q = planner.plan(dict(w.mesh), w.operand("X").spec, w.operand("A").spec, B_, J, K)
         oracle_sample(entry, lambda: ref.allreduce(q, ref.partials(q, Xc, Ac)), work,
                       f"the whole step: {q.n_units} partials X_u A_u and their rank-ordered sum")
+    # a medium batch on the same weights: 128 rows, past the split-J kernel,
+    # on the 128-row MFMA tile (8 partials [128,8192], HBM-bound on A)
+    Mm = 128
+    Xm = wl.make_operand(w.operand("X"), shape=(Mm, J)).to(dev)
+    pm = sm.sm_plan(dict(w.mesh), w.operand("X").spec, w.operand("A").spec, Mm, J, K)
+    Pm = torch.empty(pm.n_units, Mm, K, dtype=torch.float32, device=dev)
+    bxm, bpm = sm.buf(Xm), sm.buf(Pm)
+    work_m = 2.0 * (Mm * J + J * K) + 4.0 * pm.n_units * Mm * K
+    gmm = back_to_back(lambda q=ba: sm.sm_local_gemm(pm, bxm, q, bpm, sm.SM_EPI_STORE, 0, pm.n_units, stream),
+                       clock_warm=True)
+    gmm_cold = cold(lambda i: (lambda q=(ba if i == 0 else sm.buf(A.clone())):
+                               sm.sm_local_gemm(pm, bxm, q, bpm, sm.SM_EPI_STORE, 0, pm.n_units, stream)), work_m)
+    medium = rate("hbm", work_m, gmm, gmm_cold)
+    medium["workload"] = f"X[{Mm},{J}] . A[{J},{K}] on {{T:{pm.n_partials}}}: {pm.n_units} partials [{Mm},{K}] fp32"
     return {"workload": f"{w.name}: X[{B_},{J}] . A[{J},{K}], J split over {{T:{p.n_partials}}}, all-reduce",
             "fused_gemm_reduce": {**entry, "partials_bytes_not_counted": extra},
             "split_j_gemm_then_reduce_ms": round(g + r, 4),
-            "split_j_gemm_ms": round(g, 4), "reduce_ms": round(r, 4)}
+            "split_j_gemm_ms": round(g, 4), "reduce_ms": round(r, 4),
+            "medium_batch_local_gemm": medium}
 
 
 def source_digest(paths) -> str:
@@ -461,17 +480,20 @@ def main() -> int:
         if p.kase == sm.SM_CASE3:
             reduce()
 
-    def back_to_back(fn, reps, warm_ms=100.0):
+    def back_to_back(fn, reps, warm_ms=100.0, clock_warm=False):
         """Average duration of one launch: `reps` launches queued back to back
         on the kernels' stream between two HIP events.
 
         Kernels under 0.2 ms: a ~5 ms spin kernel goes first, so that all
         launches are queued before the GPU reaches them and host-side call
         overhead never shows between them; they are timed over 10x as many
-        launches. Longer kernels: about `warm_ms` of the same launches go
-        first instead, so that the timed ones run at the clock the board
-        settles at under this load (the first ~100 ms of back-to-back
-        matrix-core launches run a few percent slower)."""
+        launches. Longer kernels, and matrix-core kernels of any length
+        (clock_warm): about `warm_ms` of the same launches go first instead,
+        so that the timed ones run at the clock the board settles at under
+        this load (the first ~100 ms of back-to-back matrix-core launches run
+        a few percent slower: a one-wave K = 4096 GEMM timed after the spin
+        kernel read 8 % below its settled rate); short ones are then timed
+        over at least 20 ms of launches."""
         def once(n, n_warm):
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             torch.cuda.synchronize()
@@ -490,9 +512,9 @@ def main() -> int:
 
         fn()
         t = once(reps, 0)
-        if t < 0.2:
-            return once(10 * reps, 0)
-        return once(reps, int(warm_ms / t) + 1)
+        if t >= 0.2 or clock_warm:
+            return once(max(reps, int(20.0 / t)), int(warm_ms / t) + 1)
+        return once(10 * reps, 0)
 
     def single_launches(fn, reps):
         """(median, min) ms of `reps` launches, each between its own two HIP
@@ -604,7 +626,8 @@ def main() -> int:
     rows = None
     if not args.no_rows:
         log("bench: the other rows of the path")
-        rows = measure_rows(lambda fn: back_to_back(fn, args.steps), cold, stream, not args.no_cpu_baseline)
+        rows = measure_rows(lambda fn, **kw: back_to_back(fn, args.steps, **kw), cold, stream,
+                            not args.no_cpu_baseline)
 
     cpu = None
     if not args.no_cpu_baseline:

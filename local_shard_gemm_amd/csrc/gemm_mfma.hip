@@ -339,10 +339,42 @@ __device__ __forceinline__ void run_tile(const GemmLaunch& L, const uint16_t* __
 //    at least 15 MFMAs earlier.
 // ---------------------------------------------------------------------------
 constexpr int BK2 = 32;
-constexpr int STAGES = 5;
-constexpr int A_STAGE = BM * BK2 * 2;  // bytes
-constexpr int B_STAGE = BK2 * BN * 2;
-constexpr int STAGE_BYTES = A_STAGE + B_STAGE;
+constexpr int B_STAGE = BK2 * BN * 2;  // bytes
+
+// Geometry of the pipeline kernel for MB row blocks of 16 per wave: MB = 8,
+// the 256x256 tile above; MB = 4, a 128x256 tile for local products of at
+// most 128 rows (a batch of 65..128 tokens, whose 256-row tiles would be
+// half padding: with 128-row tiles the matrix cores do only the useful work
+// and the launch stays bound by its single pass over B).
+template <int MB>
+struct Tile {
+  static_assert(MB == 8 || MB == 4, "row blocks per wave");
+  static constexpr int BMT = 32 * MB;           // tile rows (2 waves x MB blocks of 16)
+  static constexpr int A_ST = BMT * BK2 * 2;    // A bytes per stage
+  static constexpr int ST = A_ST + B_STAGE;     // stage bytes
+  static constexpr int NST = MB == 8 ? 5 : 6;   // ring stages (160 KiB / 144 KiB)
+  static constexpr int NA = MB / 2;             // A DMA items per wave and stage
+  static constexpr int NDMA = NA + 4;           // DMA items per wave and stage
+  static constexpr int NMF = 8 * MB;            // MFMAs per wave and stage
+  static constexpr int NRD = MB + 16;           // fragment reads per wave and stage
+  // Fragment read issued after MFMA idx of a stage (-1: none). Item i < MB:
+  // A fragment i; item MB + 2 ni + t: read t of B fragment ni. Every read
+  // overwrites registers last used at least 15 MFMAs earlier (a fragment of
+  // the other set, last read by the previous stage's MFMAs).
+  static constexpr int read_at(int idx) {
+    if (MB == 8) return (idx < 48 && (idx & 1) == 0) ? idx >> 1 : -1;
+    // MB = 4 (32 MFMAs, A fragment i last used at 8i + 7, B fragment ni at
+    // 24 + ni): A0, A1 first, A2 at 6, A3 at 14, the B reads from 7 on
+    constexpr int t[32] = {0, 1, -1, -1, -1, -1, 2, 4, 5, 6, 7, 8, 9, 10, 3, 11,
+                           12, 13, 14, 15, 16, 17, 18, 19, -1, -1, -1, -1, -1, -1, -1, -1};
+    return t[idx];
+  }
+  // DMA item issued after MFMA idx (-1: none): MB = 8 on 8j + 5, MB = 4 on 5j + 3.
+  static constexpr int dma_at(int idx) {
+    if (MB == 8) return (idx & 7) == 5 ? idx >> 3 : -1;
+    return (idx % 5 == 3 && idx / 5 < NDMA) ? idx / 5 : -1;
+  }
+};
 
 typedef __attribute__((address_space(3))) char lds_char;
 typedef __attribute__((address_space(3))) void lds_void;
@@ -379,8 +411,9 @@ __device__ __forceinline__ void wait_cnt() {
   __builtin_amdgcn_s_waitcnt((vm & 0xF) | ((vm >> 4) << 14) | 0x70 | (lg << 8));
 }
 
+template <int MB>
 struct Frags {
-  bf16x8 a[8];
+  bf16x8 a[MB];
   bf16x8 b[8];
 };
 
@@ -418,20 +451,21 @@ __device__ __forceinline__ int64_t tile_row_base(const GemmLaunch& L, int row0) 
 // the bytes) and lost on single waves.
 // GUARD: a ragged tile (past row M or column N of the view); only elements
 // inside the view are stored.
-template <bool OUT_BF16, bool GELU, bool GUARD>
-__device__ __forceinline__ void store_tile_interior(const f32x4 (&acc)[8][8], void* C, const GemmLaunch& L,
+template <bool OUT_BF16, bool GELU, bool GUARD, int MB>
+__device__ __forceinline__ void store_tile_interior(const f32x4 (&acc)[MB][8], void* C, const GemmLaunch& L,
                                                     int row0, int col0, int wave) {
   const int lane = threadIdx.x & 63;
   const int wm = wave >> 1, wn = wave & 1;
+  constexpr int WR = 16 * MB;  // rows of a wave's sub-tile
   // rows / columns of this wave's sub-tile still inside the view
-  const int rmax = GUARD ? L.M - row0 - wm * 128 : 128, cmax = GUARD ? L.N - col0 - wn * 128 : 128;
+  const int rmax = GUARD ? L.M - row0 - wm * WR : WR, cmax = GUARD ? L.N - col0 - wn * 128 : 128;
   const int64_t ldc = L.ldc;
-  const int64_t base = tile_row_base(L, row0) + static_cast<int64_t>(wm * 128) * ldc + col0 + wn * 128;
+  const int64_t base = tile_row_base(L, row0) + static_cast<int64_t>(wm * WR) * ldc + col0 + wn * 128;
   const int lr = lane & 15, lc = 4 * (lane >> 4);
   const int voff = lr * static_cast<int>(ldc) + lc;
   const bool vec = L.vec_c != 0;
 #pragma unroll
-  for (int mi = 0; mi < 8; ++mi) {
+  for (int mi = 0; mi < MB; ++mi) {
     if (GUARD && mi * 16 + lr >= rmax) continue;
 #pragma unroll
     for (int ni = 0; ni < 8; ++ni) {
@@ -482,17 +516,18 @@ __device__ __forceinline__ void store_tile_interior(const f32x4 (&acc)[8][8], vo
 // 512 contiguous bytes. Stored straight from the registers, each instruction
 // writes 32 bytes to each of 16 rows, and such partial lines doubled the HBM
 // write traffic.
-template <bool GELU>
-__device__ __forceinline__ void store_tile_bf16_staged(const f32x4 (&acc)[8][8], uint16_t* ct, int64_t ldc, int wave,
+template <bool GELU, int MB>
+__device__ __forceinline__ void store_tile_bf16_staged(const f32x4 (&acc)[MB][8], uint16_t* ct, int64_t ldc, int wave,
                                                        lds_char* smem) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wm = wave >> 1, wn = wave & 1;
+  constexpr int WR = 16 * MB;  // rows of a wave's sub-tile
   wait_cnt<0, 0>();
   __builtin_amdgcn_s_barrier();  // every wave is done with the ring
   asm volatile("" ::: "memory");
 #pragma unroll
-  for (int mi = 0; mi < 8; ++mi) {
-    const int r = wm * 128 + mi * 16 + (lane & 15);
+  for (int mi = 0; mi < MB; ++mi) {
+    const int r = wm * WR + mi * 16 + (lane & 15);
 #pragma unroll
     for (int ni = 0; ni < 8; ++ni) {
       const int c = wn * 128 + ni * 16 + 4 * (lane >> 4);
@@ -511,7 +546,7 @@ __device__ __forceinline__ void store_tile_bf16_staged(const f32x4 (&acc)[8][8],
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
 #pragma unroll 4
-  for (int it = 0; it < 32; ++it) {
+  for (int it = 0; it < 32 * 2 * WR / NT; ++it) {  // 2 WR rows of 32 chunks
     const int q = tid + NT * it;
     const int r = q >> 5, ch = q & 31;
     const u32x4 v = *(lds_u32x4*)(smem + r * 512 + ((ch ^ e_swz(r)) << 4));
@@ -525,26 +560,43 @@ __device__ __forceinline__ void store_tile_bf16_staged(const f32x4 (&acc)[8][8],
 // every load stays inside the views (no bounds on the loop's loads), and
 // the duplicated data only reaches outputs past row M or column N, which
 // are not stored.
-template <bool OUT_BF16, bool GELU>
+// `wait_cnt<NDMA * n, LG>` for a count n known only at run time (n < 6).
+template <int NDMA, int LG>
+__device__ __forceinline__ void wait_stages(int n) {
+  switch (n) {
+    case 0: wait_cnt<0, LG>(); break;
+    case 1: wait_cnt<NDMA, LG>(); break;
+    case 2: wait_cnt<2 * NDMA, LG>(); break;
+    case 3: wait_cnt<3 * NDMA, LG>(); break;
+    case 4: wait_cnt<4 * NDMA, LG>(); break;
+    default: wait_cnt<5 * NDMA, LG>(); break;
+  }
+}
+
+template <bool OUT_BF16, bool GELU, int MB>
 __device__ __forceinline__ void run_tile_lds(const GemmLaunch& L, const uint16_t* __restrict__ A,
                                              const uint16_t* __restrict__ B, void* C, int row0, int col0,
                                              bool ragged, lds_char* smem) {
+  using T = Tile<MB>;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
   const int64_t lda = L.lda, ldb = L.ldb;
 
-  // ---- loader: per wave and stage 4 A items (rows (4w+i)*16 + lane/4,
-  // 64 bytes each) and 4 B items (rows (4w+i)*2 + lane/32, 512 bytes each),
-  // 1 KiB per instruction, through buffer loads whose per-lane offsets stay
-  // fixed; the k advance moves the resource base.
-  int va[4], vb[4];
+  // ---- loader: per wave and stage NA A items (rows (NA w + i) * 16 +
+  // lane/4, 64 bytes each) and 4 B items (rows (4w+i)*2 + lane/32, 512
+  // bytes each), 1 KiB per instruction, through buffer loads whose per-lane
+  // offsets stay fixed; the k advance moves the resource base.
+  int va[T::NA], vb[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int ra = (4 * wave + i) * 16 + (lane >> 2);
+  for (int i = 0; i < T::NA; ++i) {
+    const int ra = (T::NA * wave + i) * 16 + (lane >> 2);
     const int ca = (lane & 3) ^ a_swz(ra);
     const int ra_src = ragged ? min(ra, L.M - 1 - row0) : ra;
     va[i] = static_cast<int>((static_cast<int64_t>(ra_src) * lda + 8 * ca) * 2);
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
     const int rb = (4 * wave + i) * 2 + (lane >> 5);
     const int cb = (lane & 31) ^ b_swz(rb);
     const int cb_src = ragged ? min(8 * cb, ((L.N - 1) & ~7) - col0) : 8 * cb;
@@ -558,10 +610,10 @@ __device__ __forceinline__ void run_tile_lds(const GemmLaunch& L, const uint16_t
   const int64_t a_step = BK2 * 2, b_step = static_cast<int64_t>(BK2) * ldb * 2;
 
   // ---- fragment offsets inside a stage buffer.
-  // A block mi: row wm*128 + 16 mi + l%16, chunk l/16. The swizzle reads
+  // A block mi: row wm*16MB + 16 mi + l%16, chunk l/16. The swizzle reads
   // row bit 2, which comes from the lane alone, so block mi sits 1 KiB
   // after block 0.
-  const int ar = wm * 128 + (lane & 15);
+  const int ar = wm * 16 * MB + (lane & 15);
   const int a_off = ar * (BK2 * 2) + (((lane >> 4) ^ a_swz(ar)) << 4);
   // B block ni: columns wn*128 + 16 ni + 4q (q = l%4) of rows 8g + rr
   // (g = l/16, rr = (l/4)%4) for the first read and 4 rows further for the
@@ -573,16 +625,15 @@ __device__ __forceinline__ void run_tile_lds(const GemmLaunch& L, const uint16_t
 #pragma unroll
     for (int ni = 0; ni < 8; ++ni) {
       const int col = wn * 128 + ni * 16 + 4 * (lane & 3);
-      b_off[ni] = A_STAGE + kr * (BN * 2) + (((col >> 3) ^ b_swz(kr)) << 4) + ((col >> 2) & 1) * 8;
+      b_off[ni] = T::A_ST + kr * (BN * 2) + (((col >> 3) ^ b_swz(kr)) << 4) + ((col >> 2) & 1) * 8;
     }
   }
-  // Item i < 8: A fragment i; item 8 + 2 ni + t: read t of B fragment ni.
-  auto read_item = [&](Frags& F, int sb, int item) __attribute__((always_inline)) {
+  auto read_item = [&](Frags<MB>& F, int sb, int item) __attribute__((always_inline)) {
     lds_char* st = smem + sb;
-    if (item < 8) {
+    if (item < MB) {
       F.a[item] = __builtin_bit_cast(bf16x8, *(lds_u4*)(st + a_off + item * 1024));
     } else {
-      const int ni = (item - 8) >> 1, t = (item - 8) & 1;
+      const int ni = (item - MB) >> 1, t = (item - MB) & 1;
       const bf16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(st + b_off[ni] + t * 2048));
       if (t == 0)
         F.b[ni] = __builtin_shufflevector(v, F.b[ni].hi, 0, 1, 2, 3, 4, 5, 6, 7);
@@ -592,99 +643,96 @@ __device__ __forceinline__ void run_tile_lds(const GemmLaunch& L, const uint16_t
   };
   // DMA item of stage kt_load into the stage buffer at byte offset sb.
   auto dma_item = [&](int kt_load, int sb, int item) __attribute__((always_inline)) {
-    if (item < 4) {
+    if (item < T::NA) {
       const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
           (void*)(a_tile + kt_load * a_step), (short)0, 0x7fffffff, 0x00020000);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(smem + sb + (4 * wave + item) * 1024), 16, va[item], 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(smem + sb + (T::NA * wave + item) * 1024), 16, va[item],
+                                               0, 0, 0);
     } else {
       const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
           (void*)(b_tile + kt_load * b_step), (short)0, 0x7fffffff, 0x00020000);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(smem + sb + A_STAGE + (4 * wave + item - 4) * 1024), 16,
-                                               vb[item - 4], 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          r, (lds_void*)(smem + sb + T::A_ST + (4 * wave + item - T::NA) * 1024), 16, vb[item - T::NA], 0, 0, 0);
     }
   };
 
-  f32x4 acc[8][8];
+  f32x4 acc[MB][8];
 #pragma unroll
-  for (int mi = 0; mi < 8; ++mi)
+  for (int mi = 0; mi < MB; ++mi)
 #pragma unroll
     for (int ni = 0; ni < 8; ++ni) acc[mi][ni] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
   acc_fence(acc);
 
-  // One stage: 64 MFMAs on `cur`; the 24 fragment reads of the next stage
-  // ride on every other MFMA from 0 to 46 (if rd), the 8 DMA items of stage
-  // kt_load on MFMAs 8j+5 (if ld). Spread this way the stage ran 6 % faster
-  // than with the reads on MFMAs 0..23 and the DMA after them; bunching the
-  // DMA early in the stage was 5-12 % slower.
+  // One stage: NMF MFMAs on `cur`; the NRD fragment reads of the next stage
+  // (if rd) and the NDMA DMA items of stage kt_load (if ld) ride on the
+  // MFMAs that Tile<MB>::read_at / dma_at name. For the 256-row tile (64
+  // MFMAs) the reads sit on every other MFMA from 0 to 46 and the DMA on
+  // MFMAs 8j+5: spread this way the stage ran 6 % faster than with the
+  // reads on MFMAs 0..23 and the DMA after them, and bunching the DMA early
+  // in the stage was 5-12 % slower.
   // The lambdas are forced inline: inlined later, the LDS reads lost the
   // alias information that tells the compiler they do not touch the
   // in-flight LDS loads, and it waited for every load (vmcnt 0) before
   // them.
-  auto stage = [&](const Frags& cur, Frags& nxt, bool rd, int sb_rd, bool ld, int kt_load, int sb_ld) __attribute__((always_inline)) {
+  auto stage = [&](const Frags<MB>& cur, Frags<MB>& nxt, bool rd, int sb_rd, bool ld, int kt_load, int sb_ld)
+                   __attribute__((always_inline)) {
 #pragma unroll
-    for (int idx = 0; idx < 64; ++idx) {
+    for (int idx = 0; idx < T::NMF; ++idx) {
       const int mi = idx >> 3, ni = idx & 7;
       mfma16(cur.a[mi], cur.b[ni], acc[mi][ni]);
-      if (idx < 48 && (idx & 1) == 0 && rd) read_item(nxt, sb_rd, idx >> 1);
-      if ((idx & 7) == 5 && ld) dma_item(kt_load, sb_ld, idx >> 3);
+      if (T::read_at(idx) >= 0 && rd) read_item(nxt, sb_rd, T::read_at(idx));
+      if (T::dma_at(idx) >= 0 && ld) dma_item(kt_load, sb_ld, T::dma_at(idx));
       __builtin_amdgcn_sched_barrier(0);
     }
   };
 
   const int nk = L.K / BK2;
-  constexpr int RING = STAGES * STAGE_BYTES;
-  Frags F[2];
-  // prologue: stages 0..4 in flight, then stage 0's fragments
+  constexpr int NST = T::NST;
+  constexpr int RING = NST * T::ST;
+  Frags<MB> F[2];
+  // prologue: stages 0..NST-1 in flight, then stage 0's fragments
 #pragma unroll
-  for (int p = 0; p < STAGES; ++p)
+  for (int p = 0; p < NST; ++p)
     if (p < nk) {
 #pragma unroll
-      for (int it = 0; it < 8; ++it) dma_item(p, p * STAGE_BYTES, it);
+      for (int it = 0; it < T::NDMA; ++it) dma_item(p, p * T::ST, it);
     }
-  if (nk > 4) wait_cnt<32, 15>();
-  else if (nk == 4) wait_cnt<24, 15>();
-  else if (nk == 3) wait_cnt<16, 15>();
-  else if (nk == 2) wait_cnt<8, 15>();
-  else wait_cnt<0, 15>();
+  wait_stages<T::NDMA, 15>(min(nk, NST) - 1);  // stage 0 landed
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
   if (nk > 0) {
 #pragma unroll
-    for (int i = 0; i < 24; ++i) read_item(F[0], 0, i);
+    for (int i = 0; i < T::NRD; ++i) read_item(F[0], 0, i);
   }
 
-  int sb_cur = 0;             // buffer of stage kt
-  int sb_rd = STAGE_BYTES;    // buffer of stage kt+1
+  int sb_cur = 0;        // buffer of stage kt
+  int sb_rd = T::ST;     // buffer of stage kt+1
   // Iteration kt: the MFMAs of stage kt on F[kt % 2]; stage kt+1's
-  // fragments into the other set; stage kt+5 into stage kt's buffer. That
+  // fragments into the other set; stage kt+NST into stage kt's buffer. That
   // buffer is free: its fragments were read in iteration kt-1, and every
   // wave waited for its reads (lgkmcnt 0) before this iteration's barrier.
-  // Loads run 4 stages ahead.
+  // Loads run NST-1 stages ahead.
   auto iter = [&](auto parity_c, int kt, bool steady) __attribute__((always_inline)) {
     constexpr int P = decltype(parity_c)::value;  // kt % 2
     const bool rd = steady || kt + 1 < nk;
-    const bool ld = steady || kt + STAGES < nk;
+    const bool ld = steady || kt + NST < nk;
     __builtin_amdgcn_sched_barrier(0);
-    // stage kt+1 landed; stages kt+2 .. kt+4 may still be in flight
-    if (steady || kt + 4 < nk)
-      wait_cnt<24, 0>();
-    else if (kt + 3 < nk)
-      wait_cnt<16, 0>();
-    else if (kt + 2 < nk)
-      wait_cnt<8, 0>();
+    // stage kt+1 landed; stages kt+2 .. kt+NST-1 may still be in flight
+    if (steady)
+      wait_cnt<(NST - 2) * T::NDMA, 0>();
     else
-      wait_cnt<0, 0>();
+      wait_stages<T::NDMA, 0>(max(0, min(nk - 1, kt + NST - 1) - (kt + 1)));
     asm volatile("" ::: "memory");
     if (rd) __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
-    stage(F[P], F[P ^ 1], rd, sb_rd, ld, kt + STAGES, sb_cur);
+    stage(F[P], F[P ^ 1], rd, sb_rd, ld, kt + NST, sb_cur);
     sb_cur = sb_rd;
-    sb_rd = sb_rd + STAGE_BYTES == RING ? 0 : sb_rd + STAGE_BYTES;
+    sb_rd = sb_rd + T::ST == RING ? 0 : sb_rd + T::ST;
   };
 
   int kt = 0;
-  for (; kt + 1 + STAGES < nk; kt += 2) {
+  for (; kt + 1 + NST < nk; kt += 2) {
     iter(std::integral_constant<int, 0>{}, kt, true);
     iter(std::integral_constant<int, 1>{}, kt + 1, true);
   }
@@ -698,7 +746,7 @@ __device__ __forceinline__ void run_tile_lds(const GemmLaunch& L, const uint16_t
   // K tail (K % 32 columns of A, rows of B): one more stage, loaded through
   // registers with every element at or past K (and past the view's rows of
   // A or columns of B) read as zero, and written into ring buffer 0 in the
-  // layout the buffer loads produce; then its 64 MFMAs.
+  // layout the buffer loads produce; then its MFMAs.
   const int k_tail = L.K - nk * BK2;
   if (k_tail > 0) {
     wait_cnt<0, 0>();
@@ -706,8 +754,8 @@ __device__ __forceinline__ void run_tile_lds(const GemmLaunch& L, const uint16_t
     asm volatile("" ::: "memory");
     const int kb = nk * BK2;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int q = tid + NT * j;  // A: 256 rows x 4 chunks of 8 k
+    for (int j = 0; j < T::BMT * 4 / NT; ++j) {
+      const int q = tid + NT * j;  // A: BMT rows x 4 chunks of 8 k
       const int r = q >> 2, c = q & 3;
       const int row = row0 + min(r, L.M - 1 - row0);
       uint32_t w[4];
@@ -733,33 +781,33 @@ __device__ __forceinline__ void run_tile_lds(const GemmLaunch& L, const uint16_t
         const uint32_t lo = (k < L.K && n0 < L.N) ? pb[0] : 0u, hi = (k < L.K && n0 + 1 < L.N) ? pb[1] : 0u;
         w[e] = lo | (hi << 16);
       }
-      *(lds_u32x4*)(smem + A_STAGE + rb * (BN * 2) + ((cb ^ b_swz(rb)) << 4)) = u32x4{w[0], w[1], w[2], w[3]};
+      *(lds_u32x4*)(smem + T::A_ST + rb * (BN * 2) + ((cb ^ b_swz(rb)) << 4)) = u32x4{w[0], w[1], w[2], w[3]};
     }
     wait_cnt<0, 0>();
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
 #pragma unroll
-    for (int i = 0; i < 24; ++i) read_item(F[0], 0, i);
+    for (int i = 0; i < T::NRD; ++i) read_item(F[0], 0, i);
     wait_cnt<0, 0>();
 #pragma unroll
-    for (int mi = 0; mi < 8; ++mi)
+    for (int mi = 0; mi < MB; ++mi)
 #pragma unroll
       for (int ni = 0; ni < 8; ++ni) mfma16(F[0].a[mi], F[0].b[ni], acc[mi][ni]);
     acc_drain(acc);
   }
 
   if (ragged) {
-    store_tile_interior<OUT_BF16, GELU, true>(acc, C, L, row0, col0, wave);
+    store_tile_interior<OUT_BF16, GELU, true, MB>(acc, C, L, row0, col0, wave);
   } else if constexpr (OUT_BF16) {
     // whole rows through LDS when the tile's rows start on 16 bytes (the
     // view's start; ldc is a multiple of 8 and col0 of 256)
     uint16_t* ct = static_cast<uint16_t*>(C) + tile_row_base(L, row0) + col0;
     if ((reinterpret_cast<uintptr_t>(ct) & 15) == 0)
-      store_tile_bf16_staged<GELU>(acc, ct, L.ldc, wave, smem);
+      store_tile_bf16_staged<GELU, MB>(acc, ct, L.ldc, wave, smem);
     else
-      store_tile_interior<OUT_BF16, GELU, false>(acc, C, L, row0, col0, wave);
+      store_tile_interior<OUT_BF16, GELU, false, MB>(acc, C, L, row0, col0, wave);
   } else {
-    store_tile_interior<OUT_BF16, GELU, false>(acc, C, L, row0, col0, wave);
+    store_tile_interior<OUT_BF16, GELU, false, MB>(acc, C, L, row0, col0, wave);
   }
 }
 
@@ -768,33 +816,35 @@ __device__ __forceinline__ void run_tile_lds(const GemmLaunch& L, const uint16_t
 // views and whose stores are guarded; a K that is not a multiple of 32 ends
 // with a zero-filled tail stage. Every view is 16-byte aligned
 // (all_tiles_edge false).
-template <bool OUT_BF16, bool GELU>
+// L.tiles_m counts tiles of Tile<MB>::BMT rows.
+template <bool OUT_BF16, bool GELU, int MB>
 __global__ __launch_bounds__(NT, 1) void gemm_bf16_mfma_kernel(const GemmLaunch L) {
-  __shared__ __attribute__((aligned(1024))) char smem[STAGES * STAGE_BYTES];
+  constexpr int BMT = Tile<MB>::BMT;
+  __shared__ __attribute__((aligned(1024))) char smem[Tile<MB>::NST * Tile<MB>::ST];
   const int VR = L.n_units * L.tiles_m;
   const int T = VR * L.tiles_n;
   int vr, vc;
   tile_of(blockIdx.x, T, VR, L.tiles_n, &vr, &vc);
   const int unit = vr / L.tiles_m;
-  const int row0 = (vr - unit * L.tiles_m) * BM;
+  const int row0 = (vr - unit * L.tiles_m) * BMT;
   const int col0 = vc * BN;
-  const bool ragged = row0 + BM > L.M || col0 + BN > L.N;
+  const bool ragged = row0 + BMT > L.M || col0 + BN > L.N;
   const GemmUnitPtrs U = L.u[unit];
-  run_tile_lds<OUT_BF16, GELU>(L, U.a, U.b, U.c, row0, col0, ragged, (lds_char*)smem);
+  run_tile_lds<OUT_BF16, GELU, MB>(L, U.a, U.b, U.c, row0, col0, ragged, (lds_char*)smem);
 }
 
 // The MFMA kernel takes every tile unless a view is not 16-byte aligned (or
 // the last row of a B view leaves no room for a 16-byte chunk past column
 // N, which the host folds into vec_ok), a lane's byte offset inside a tile's buffer
-// resource (up to 255 rows of A, 31 rows of B) or a lane's element offset
+// resource (up to BMT-1 rows of A, 31 rows of B) or a lane's element offset
 // inside an output tile (31 rows of C) would not fit in 31 bits, or a row
 // split of the output does not fall on tile boundaries. Then every tile goes
 // to the edge kernel.
-__host__ __device__ __forceinline__ bool all_tiles_edge(const GemmLaunch& L) {
+__host__ __device__ __forceinline__ bool all_tiles_edge(const GemmLaunch& L, int bmt) {
   constexpr int64_t kMaxOffset = int64_t{1} << 31;
-  return !L.vec_ok || (static_cast<int64_t>(BM - 1) * L.lda + BK2) * 2 >= kMaxOffset ||
+  return !L.vec_ok || (static_cast<int64_t>(bmt - 1) * L.lda + BK2) * 2 >= kMaxOffset ||
          (static_cast<int64_t>(BK2 - 1) * L.ldb + BN) * 2 >= kMaxOffset || L.ldc * 32 >= kMaxOffset ||
-         (L.split_rows < L.M && L.split_rows % BM != 0);
+         (L.split_rows < L.M && L.split_rows % bmt != 0);
 }
 
 // Edge kernel: every tile of the launch (all_tiles_edge). Loads outside the
@@ -809,11 +859,18 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16_mfma_edge_kernel(const GemmLa
   run_tile<true, OUT_BF16, GELU>(L, U.a, U.b, U.c, tm * BM, tn * BN, lds);
 }
 
+// Local products of at most 128 rows take the 128-row tile (Tile<4>),
+// taller ones the 256-row tile (Tile<8>).
 template <bool OUT_BF16, bool GELU>
 hipError_t launch_variant(const GemmLaunch& L, hipStream_t s) {
-  if (!all_tiles_edge(L)) {
+  if (L.M <= Tile<4>::BMT && !all_tiles_edge(L, Tile<4>::BMT)) {
+    GemmLaunch L4 = L;
+    L4.tiles_m = (L.M + Tile<4>::BMT - 1) / Tile<4>::BMT;
+    const int T = L4.n_units * L4.tiles_m * L4.tiles_n;
+    hipLaunchKernelGGL((gemm_bf16_mfma_kernel<OUT_BF16, GELU, 4>), dim3(T), dim3(NT), 0, s, L4);
+  } else if (L.M > Tile<4>::BMT && !all_tiles_edge(L, Tile<8>::BMT)) {
     const int T = L.n_units * L.tiles_m * L.tiles_n;
-    hipLaunchKernelGGL((gemm_bf16_mfma_kernel<OUT_BF16, GELU>), dim3(T), dim3(NT), 0, s, L);
+    hipLaunchKernelGGL((gemm_bf16_mfma_kernel<OUT_BF16, GELU, 8>), dim3(T), dim3(NT), 0, s, L);
   } else {
     hipLaunchKernelGGL((gemm_bf16_mfma_edge_kernel<OUT_BF16, GELU>), dim3(L.tiles_m * L.tiles_n, L.n_units), dim3(NT),
                        0, s, L);
