@@ -360,6 +360,7 @@ def measure_skinny(back_to_back, cold, stream, with_oracle: bool = False) -> dic
     g = back_to_back(lambda: sm.sm_local_gemm(p, bx, ba, bp, sm.SM_EPI_STORE, 0, p.n_units, stream))
     r = back_to_back(lambda: sm.sm_reduce_partials(p, bp, bo, sm.SM_ALLREDUCE, 0, p.n_groups, stream))
     entry = rate("hbm", work, f, f_cold)
+    entry["traffic"] = recorded_traffic("fused", w.name)
     if with_oracle:
         from oracle import planner, reference as ref
 
@@ -379,6 +380,7 @@ def measure_skinny(back_to_back, cold, stream, with_oracle: bool = False) -> dic
     gmm_cold = cold(lambda i: (lambda q=(ba if i == 0 else sm.buf(A.clone())):
                                sm.sm_local_gemm(pm, bxm, q, bpm, sm.SM_EPI_STORE, 0, pm.n_units, stream)), work_m)
     medium = rate("hbm", work_m, gmm, gmm_cold)
+    medium["traffic"] = recorded_traffic("medium", w.name)
     medium["workload"] = f"X[{Mm},{J}] . A[{J},{K}] on {{T:{pm.n_partials}}}: {pm.n_units} partials [{Mm},{K}] fp32"
     return {"workload": f"{w.name}: X[{B_},{J}] . A[{J},{K}], J split over {{T:{p.n_partials}}}, all-reduce",
             "fused_gemm_reduce": {**entry, "partials_bytes_not_counted": extra},
@@ -402,9 +404,9 @@ def recorded_traffic(launch: str, workload: str):
     """HBM bytes per launch measured by rocprofv3 counters (FETCH_SIZE and
     WRITE_SIZE, scaled by a plain-copy calibration), as recorded in a
     `traffic-record:` line of a counter summary under profiles/. Returns None
-    when there is no record for this launch ("gemm", "reduce" or "fused") and
-    workload, or when the kernel's sources changed after the counters were
-    taken."""
+    when there is no record for this launch ("gemm", "reduce", "fused" or
+    "medium") and workload, or when the kernel's sources changed after the
+    counters were taken."""
     import glob
 
     for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "*.md"))):
