@@ -370,7 +370,8 @@ def measure_skinny(back_to_back, cold, stream, with_oracle: bool = False) -> dic
     # a medium batch on the same weights: 128 rows, past the split-J kernel,
     # on the 128-row MFMA tile (8 partials [128,8192], HBM-bound on A)
     Mm = 128
-    Xm = wl.make_operand(w.operand("X"), shape=(Mm, J)).to(dev)
+    Xm_cpu = wl.make_operand(w.operand("X"), shape=(Mm, J))
+    Xm = Xm_cpu.to(dev)
     pm = sm.sm_plan(dict(w.mesh), w.operand("X").spec, w.operand("A").spec, Mm, J, K)
     Pm = torch.empty(pm.n_units, Mm, K, dtype=torch.float32, device=dev)
     bxm, bpm = sm.buf(Xm), sm.buf(Pm)
@@ -381,6 +382,10 @@ def measure_skinny(back_to_back, cold, stream, with_oracle: bool = False) -> dic
                                sm.sm_local_gemm(pm, bxm, q, bpm, sm.SM_EPI_STORE, 0, pm.n_units, stream)), work_m)
     medium = rate("hbm", work_m, gmm, gmm_cold)
     medium["traffic"] = recorded_traffic("medium", w.name)
+    if with_oracle:
+        qm = planner.plan(dict(w.mesh), w.operand("X").spec, w.operand("A").spec, Mm, J, K)
+        oracle_sample(medium, lambda: ref.partials(qm, Xm_cpu, Ac), work_m,
+                      f"the whole launch: {qm.n_units} partials X_u A_u of [{Mm},{qm.a_local[1]}]x[{qm.a_local[1]},{K}]")
     medium["workload"] = f"X[{Mm},{J}] . A[{J},{K}] on {{T:{pm.n_partials}}}: {pm.n_units} partials [{Mm},{K}] fp32"
     return {"workload": f"{w.name}: X[{B_},{J}] . A[{J},{K}], J split over {{T:{p.n_partials}}}, all-reduce",
             "fused_gemm_reduce": {**entry, "partials_bytes_not_counted": extra},
