@@ -265,21 +265,28 @@ int32_t sm_local_gemm_reduce(const sm_plan_t* plan, const sm_buf* A, const sm_bu
                              const sm_buf* out, int32_t mode, int32_t group_begin,
                              int32_t group_count, void* stream);
 
-/* Bytes of device workspace sm_local_gemm_reduce_ws needs for group_count
- * groups of a case-3 plan: 0 when the local products have more than 64
- * rows, else the arrival counters followed by the N partials of each group
- * (see below). Errors: SM_ERR_CASE unless case 3, SM_ERR_ARG for a
- * group_count outside [1, n_groups]. */
+/* Bytes of device workspace sm_local_gemm_reduce_ws uses for group_count
+ * groups of a case-3 plan: for local products of at most 64 rows the
+ * arrival counters followed by the N partials of each group (required);
+ * for taller products whose single launch would have fewer than 256 output
+ * tiles, the N partials of each group (optional, see below); else 0.
+ * Errors: SM_ERR_CASE unless case 3, SM_ERR_ARG for a group_count outside
+ * [1, n_groups]. */
 int32_t sm_gemm_reduce_workspace(const sm_plan_t* plan, int32_t group_count, int64_t* bytes);
 
 /* sm_local_gemm_reduce for every local-product height, with a
  * caller-provided workspace (mbrenndoerfer.com "Row Parallelism": each rank
  * forms Z_i = X_i A_i and the output is their sum Y = sum_i X_i A_i;
  * semiaifoundry.com "The mechanism", step 4). Local products of more than
- * 64 rows run exactly as in sm_local_gemm_reduce and leave the workspace
- * untouched (it may be NULL then). Local products of at most 64 rows (a
- * skinny batch) run the split-J streaming kernel with the reduction fused
- * into it, in one launch per 64 units:
+ * 64 rows run as in sm_local_gemm_reduce (one launch over the group's whole
+ * J), unless that launch would have fewer than 256 output tiles and the
+ * workspace holds the N partials of each group: then the N units' products
+ * run in parallel into the workspace and a second launch sums them in rank
+ * order (exactly sm_local_gemm + sm_reduce_partials; on floats this differs
+ * from the single launch by fp32 rounding only). The workspace may be NULL
+ * or smaller for these plans. Local products of at most 64 rows (a skinny
+ * batch) run the split-J streaming kernel with the reduction fused into it,
+ * in one launch per 64 units:
  *  - every workgroup (one unit y of group g, one block of 256 output
  *    columns) writes its partial P_{g,y} into the workspace and counts
  *    itself in at the counter of its (group, column block);
@@ -310,15 +317,17 @@ int32_t sm_local_gemm_reduce_ws(const sm_plan_t* plan, const sm_buf* A, const sm
  * loops, harnesses that forbid allocation. The call allocates nothing (no
  * hipMalloc, hipFree or allocating library routine). Skinny products keep
  * their counters and partials in the library's static device array
- * (64 KiB of counters + 16 MiB of partials, held by every GPU the library
+ * (64 KiB of counters + 32 MiB of partials, held by every GPU the library
  * runs on until the process ends); a call that needs more is refused with
  * SM_ERR_SHAPE before anything is launched (use sm_local_gemm_reduce_ws).
  * The first call on a device also enqueues, on `stream`, the clearing of
  * that device's counters; every completed call leaves them zero. All calls
  * on one GPU share the array: calls that overlap in time (other streams
  * without synchronisation, other threads) race. Products of more than 64
- * rows need no scratch and run as sm_local_gemm_reduce. Results are bit for
- * bit those of sm_local_gemm_reduce_ws. Errors as sm_local_gemm_reduce_ws. */
+ * rows use the scratch as sm_local_gemm_reduce_ws uses its workspace when
+ * their partials fit in it, else run as sm_local_gemm_reduce. Results are
+ * bit for bit those of sm_local_gemm_reduce_ws with a workspace of the
+ * same capacity. Errors as sm_local_gemm_reduce_ws. */
 int32_t sm_local_gemm_reduce_noalloc(const sm_plan_t* plan, const sm_buf* A, const sm_buf* B,
                                      const sm_buf* out, int32_t mode, int32_t group_begin,
                                      int32_t group_count, void* stream);

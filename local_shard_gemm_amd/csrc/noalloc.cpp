@@ -27,11 +27,11 @@
 #include "internal.h"
 #include "kernels.h"
 
-// Room for the partials of one call: 16 MiB (for example N = 8 ranks x 64
+// Room for the partials of one call: 32 MiB (for example N = 8 ranks x 128
 // rows x 8192 float32 columns), behind 64 KiB of counters (16384 column
 // blocks over all groups of the call).
 constexpr int64_t kScratchCounterBytes = int64_t{64} << 10;
-constexpr int64_t kScratchPartBytes = int64_t{16} << 20;
+constexpr int64_t kScratchPartBytes = int64_t{32} << 20;
 constexpr int64_t kScratchBytes = kScratchCounterBytes + kScratchPartBytes;
 
 static __device__ __align__(256) unsigned char scratch[kScratchBytes];
@@ -81,9 +81,9 @@ extern "C" int32_t sm_local_gemm_reduce_noalloc(const sm_plan_t* plan, const sm_
   int32_t st = gemm_reduce_impl(plan, A, B, out, mode, group_begin, group_count, sc, stream, nullptr);
   if (st) return st;
   const bool skinny = plan->c_local[0] <= kSkinnyMaxM;
-  if (skinny) {
-    const ReduceWorkspace w = reduce_workspace(*plan, group_count);
-    if (w.counter_bytes > kScratchCounterBytes || w.part_bytes > kScratchPartBytes)
+  const ReduceWorkspace w = reduce_workspace(*plan, group_count);
+  if (skinny || (w.two_pass && w.part_bytes <= kScratchPartBytes)) {
+    if (skinny && (w.counter_bytes > kScratchCounterBytes || w.part_bytes > kScratchPartBytes))
       return fail(SM_ERR_SHAPE, "the call needs " + std::to_string(w.counter_bytes) + " bytes of counters and " +
                                     std::to_string(w.part_bytes) + " bytes of partials; the static scratch holds " +
                                     std::to_string(kScratchCounterBytes) + " and " +
@@ -98,7 +98,9 @@ extern "C" int32_t sm_local_gemm_reduce_noalloc(const sm_plan_t* plan, const sm_
     sc.parts = reinterpret_cast<float*>(static_cast<unsigned char*>(base) + kScratchCounterBytes);
     sc.part_cap = kScratchPartBytes;
   } else {
-    sc.kind = ReduceScratch::kNone;  // products of more than 64 rows need no scratch
+    // taller products: one launch over the whole J, no scratch (also when a
+    // few-tile product's partials do not fit the scratch)
+    sc.kind = ReduceScratch::kNone;
   }
   return gemm_reduce_impl(plan, A, B, out, mode, group_begin, group_count, sc, stream,
                           "sm_local_gemm_reduce_noalloc launch");

@@ -317,8 +317,14 @@ def test_skinny_fused_reduce_workspace_and_validation():
     g2 = sm.sm_plan({"X": 2, "T": 4}, "P('X', 'T')", "P('T', None)", 48, 512, 300)
     assert sm.sm_gemm_reduce_workspace(g2, 1) == 256 + 4 * 24 * 300 * 4
     assert sm.sm_gemm_reduce_workspace(g2) == 256 + 2 * 4 * 24 * 300 * 4
-    big = sm.sm_plan({"T": 2}, "P(None, 'T')", "P('T', None)", 65, 128, 64)  # tile kernel: none needed
-    assert sm.sm_gemm_reduce_workspace(big) == 0
+    # taller products: the partials when a single launch would have fewer
+    # than 256 tiles (here 1), none when it fills the GPU (the down-projection:
+    # 4 groups x 8 x 32 tiles)
+    few = sm.sm_plan({"T": 2}, "P(None, 'T')", "P('T', None)", 65, 128, 64)
+    assert sm.sm_gemm_reduce_workspace(few) == 2 * 65 * 64 * 4
+    dp = sm.sm_plan({"X": 4, "Y": 2}, "P('X', 'Y')", "P('Y', None)", 8192, 28672, 8192)
+    assert sm.sm_gemm_reduce_workspace(dp) == 0
+    assert sm.sm_gemm_reduce_workspace(dp, 1) == 0  # one group: 256 tiles
     assert _err(sm.sm_gemm_reduce_workspace, sk, 2) == sm.SM_ERR_ARG
     assert _err(sm.sm_gemm_reduce_workspace, sm.sm_plan({"X": 2}, "P('X', None)", "P()", 64, 128, 64)) \
         == sm.SM_ERR_CASE

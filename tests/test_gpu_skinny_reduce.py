@@ -12,7 +12,7 @@ import local_shard_gemm_amd as sm
 import workloads as wl
 from oracle import planner, reference as ref
 
-from hip_cases import DEV, REL_TOL, f32_bits_equal, guard_intact, guarded, run_partials, say, to_dev
+from hip_cases import DEV, FREIVALDS_FLOAT_TOL, REL_TOL, f32_bits_equal, guard_intact, guarded, run_partials, say, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -173,3 +173,85 @@ def test_full_skinny_fused_reduce(integer):
         err = ref.rel_frobenius(got, s)
         say("skinny fused rel err", err)
         assert err <= REL_TOL
+
+
+# ------------------------------------------- taller products with few tiles
+
+FEW_TILES = [
+    ({"T": 8}, "P(None, 'T')", "P('T', None)", 128, 8 * 256, 1024),        # 4 tiles of 128 rows
+    ({"X": 2, "T": 4}, "P('X', 'T')", "P('T', None)", 2 * 96, 4 * 100, 296),  # two groups, ragged K and N
+    ({"T": 2}, "P(None, 'T')", "P('T', None)", 65, 2 * 64, 512),          # one ragged row tile
+    ({"T": 4}, "P(None, 'T')", "P('T', None)", 300, 4 * 64, 256),          # 256-row tiles, ragged
+]
+
+
+@pytest.mark.parametrize("case", FEW_TILES, ids=lambda c: f"{c[3]}x{c[4]}x{c[5]}")
+@pytest.mark.parametrize("mode", [sm.SM_ALLREDUCE, sm.SM_REDUCESCATTER], ids=["AR", "RS"])
+def test_few_tile_products_reduce_through_the_workspace(case, mode):
+    """Local products taller than 64 rows whose single launch over the whole
+    J would have few tiles: with a workspace, the units' products and their
+    rank-ordered sum (two launches), bit for bit the oracle's rank-order sums
+    on integers and bit for bit sm_local_gemm + sm_reduce_partials; without
+    one, the single launch, also exact on integers."""
+    mesh, sa, sb, I, J, K = case
+    say("case: few-tile fused", case, mode)
+    A = wl.random_ints((I, J), 821 + I)
+    B = wl.random_ints((J, K), 822 + K)
+    p = sm.sm_plan(mesh, sa, sb, I, J, K)
+    q = planner.plan(mesh, sa, sb, I, J, K)
+    m, n = q.c_local
+    N = q.n_partials
+    if mode == sm.SM_REDUCESCATTER and m % N:
+        return
+    nbytes = sm.sm_gemm_reduce_workspace(p)
+    assert nbytes == q.n_groups * N * m * (-(-n // 4) * 4) * 4
+    Ad, Bd = to_dev(A), to_dev(B)
+    ws = torch.full((nbytes // 4,), float("nan"), device=DEV)
+    fg, g = guarded((I, K), torch.float32)
+    sm.sm_local_gemm_reduce_ws(p, sm.buf(Ad), sm.buf(Bd), sm.buf(g), ws, mode)
+    one = torch.full((I, K), float("nan"), device=DEV)
+    sm.sm_local_gemm_reduce_ws(p, sm.buf(Ad), sm.buf(Bd), sm.buf(one), None, mode)
+    _, P = run_partials(p, Ad, Bd)
+    two = torch.empty(I, K, device=DEV)
+    sm.sm_reduce_partials(p, sm.buf(P), sm.buf(two), mode)
+    torch.cuda.synchronize()
+    parts = [ref.unit_partial(q, A, B, u) for u in range(q.n_units)]
+    want = ref.gather(q, ref.allreduce(q, parts))
+    assert f32_bits_equal(g.cpu().numpy(), want)
+    assert guard_intact(fg, g.numel())
+    assert torch.equal(g, two)
+    assert f32_bits_equal(one.cpu().numpy(), want)
+
+
+def test_full_medium_batch_fused_reduce():
+    """A 128-row batch on the skinny workload's weights (float): the
+    workspace call runs the 8 units' products and their rank-ordered sum,
+    bit for bit sm_local_gemm + sm_reduce_partials; sampled rows within the
+    float tolerance of the oracle's rank-order sums, the whole output by
+    Freivalds' test; the single launch (no workspace) within the same
+    bounds."""
+    w = wl.get("skinny")
+    say("case: full medium fused")
+    X = wl.make_operand(w.operand("X"), shape=(128, 28672))
+    A = wl.make_operand(w.operand("A"))
+    args = (dict(w.mesh), w.operand("X").spec, w.operand("A").spec, 128, 28672, 8192)
+    p, q = sm.sm_plan(*args), planner.plan(*args)
+    Xd, Ad = to_dev(X), to_dev(A)
+    ws = torch.empty(sm.sm_gemm_reduce_workspace(p) // 4, device=DEV)
+    out = torch.empty(128, 8192, device=DEV)
+    sm.sm_local_gemm_reduce_ws(p, sm.buf(Xd), sm.buf(Ad), sm.buf(out), ws, sm.SM_ALLREDUCE)
+    _, P = run_partials(p, Xd, Ad)
+    two = torch.empty(128, 8192, device=DEV)
+    sm.sm_reduce_partials(p, sm.buf(P), sm.buf(two), sm.SM_ALLREDUCE)
+    one = torch.empty(128, 8192, device=DEV)
+    sm.sm_local_gemm_reduce(p, sm.buf(Xd), sm.buf(Ad), sm.buf(one), sm.SM_ALLREDUCE)
+    torch.cuda.synchronize()
+    assert torch.equal(out, two)
+    rows = [0, 1, 63, 64, 127]
+    (s,) = ref.allreduce(q, [ref.unit_partial(q, X, A, u, rows=rows) for u in range(q.n_units)])
+    for name, got in (("workspace", out), ("single launch", one)):
+        g = got.cpu().numpy()
+        err = ref.rel_frobenius(g[rows], s)
+        fr = ref.freivalds(X, (0, 0, 128, 28672), A, (0, 0, 28672, 8192), g, trials=1, ints=False)
+        say("medium fused", name, "rows rel err", err, "freivalds", fr)
+        assert err <= REL_TOL and fr <= FREIVALDS_FLOAT_TOL

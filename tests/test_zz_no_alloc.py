@@ -60,25 +60,51 @@ def test_noalloc_two_calls_then_smaller():
     assert f32_bits_equal(a3.cpu().numpy(), ref.allreduce(q3, parts)[0])
 
 
-def test_noalloc_refuses_calls_beyond_the_scratch_and_runs_tile_products():
+def test_noalloc_refuses_calls_beyond_the_scratch_and_runs_taller_products():
     say("case: noalloc limits")
-    # 8 partials of [64, 8200] float32 need 16.8 MB of partials: refused
-    p = sm.sm_plan({"T": 8}, "P(None, 'T')", "P('T', None)", 64, 8 * 16, 8200)
+    # 8 partials of [64, 16400] float32 need 33.6 MB of partials: refused
+    p = sm.sm_plan({"T": 8}, "P(None, 'T')", "P('T', None)", 64, 8 * 16, 16400)
     X = to_dev(wl.random_ints((64, 128), 911))
-    A = to_dev(wl.random_ints((128, 8200), 912))
-    out = torch.full((64, 8200), float("nan"), device=DEV)
+    A = to_dev(wl.random_ints((128, 16400), 912))
+    out = torch.full((64, 16400), float("nan"), device=DEV)
     with pytest.raises(sm.ShardmmError) as ei:
         sm.sm_local_gemm_reduce_noalloc(p, sm.buf(X), sm.buf(A), sm.buf(out))
     assert ei.value.status == sm.SM_ERR_SHAPE and "static scratch" in str(ei.value)
     torch.cuda.synchronize()
     assert bool(torch.isnan(out).all())
-    # more than 64 rows: the tile kernel, no scratch, same as sm_local_gemm_reduce
+    # more than 64 rows with few tiles: the units' products on the scratch,
+    # as sm_local_gemm_reduce_ws does them with its workspace
     p = sm.sm_plan({"Y": 2}, "P(None, 'Y')", "P('Y', None)", 128, 2 * 128, 256)
-    X = to_dev(wl.random_ints((128, 256), 913))
-    A = to_dev(wl.random_ints((256, 256), 914))
+    X = to_dev(wl.random_normal((128, 256), 913))
+    A = to_dev(wl.random_normal((256, 256), 914))
     a = torch.empty(128, 256, device=DEV)
     b = torch.empty(128, 256, device=DEV)
+    ws = torch.empty(sm.sm_gemm_reduce_workspace(p) // 4, device=DEV)
     sm.sm_local_gemm_reduce_noalloc(p, sm.buf(X), sm.buf(A), sm.buf(a), sm.SM_REDUCESCATTER)
-    sm.sm_local_gemm_reduce(p, sm.buf(X), sm.buf(A), sm.buf(b), sm.SM_REDUCESCATTER)
+    sm.sm_local_gemm_reduce_ws(p, sm.buf(X), sm.buf(A), sm.buf(b), ws, sm.SM_REDUCESCATTER)
     torch.cuda.synchronize()
     assert torch.equal(a, b)
+    # partials beyond the scratch: the single launch, as sm_local_gemm_reduce
+    p = sm.sm_plan({"T": 8}, "P(None, 'T')", "P('T', None)", 128, 8 * 64, 16384)  # 8 x 8 MiB of partials
+    X = to_dev(wl.random_ints((128, 512), 915))
+    A = to_dev(wl.random_ints((512, 16384), 916))
+    a = torch.empty(128, 16384, device=DEV)
+    b = torch.empty(128, 16384, device=DEV)
+    sm.sm_local_gemm_reduce_noalloc(p, sm.buf(X), sm.buf(A), sm.buf(a))
+    sm.sm_local_gemm_reduce(p, sm.buf(X), sm.buf(A), sm.buf(b))
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+def test_noalloc_medium_batch_on_the_scratch():
+    """A 128-row batch on the skinny workload's weights (8 partials of
+    [128, 8192] float32, 32 MiB: the whole scratch): bit for bit the
+    workspace call, twice in a row."""
+    w = wl.get("skinny")
+    say("case: noalloc medium batch")
+    X = to_dev(wl.make_operand(w.operand("X"), shape=(128, 28672)))
+    A = to_dev(wl.make_operand(w.operand("A")))
+    p = sm.sm_plan(dict(w.mesh), w.operand("X").spec, w.operand("A").spec, 128, 28672, 8192)
+    for mode in (sm.SM_ALLREDUCE, sm.SM_REDUCESCATTER):
+        a, b = _both(p, X, A, mode, (128, 8192))
+        assert torch.equal(a, b)
