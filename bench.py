@@ -387,11 +387,32 @@ def measure_skinny(back_to_back, cold, stream, with_oracle: bool = False) -> dic
         oracle_sample(medium, lambda: ref.partials(qm, Xm_cpu, Ac), work_m,
                       f"the whole launch: {qm.n_units} partials X_u A_u of [{Mm},{qm.a_local[1]}]x[{qm.a_local[1]},{K}]")
     medium["workload"] = f"X[{Mm},{J}] . A[{J},{K}] on {{T:{pm.n_partials}}}: {pm.n_units} partials [{Mm},{K}] fp32"
+    # the medium batch's whole step with its sum (sm_local_gemm_reduce_ws:
+    # the 8 units' products into the workspace, then their rank-ordered
+    # sum); algorithmic bytes as for the skinny step: X, A and the output
+    wsm = torch.empty(sm.sm_gemm_reduce_workspace(pm) // 4, dtype=torch.float32, device=dev)
+    outm = torch.empty(Mm, K, dtype=torch.float32, device=dev)
+    bom = sm.buf(outm)
+    work_ms = 2.0 * (Mm * J + J * K) + 4.0 * Mm * K
+    mstep = back_to_back(lambda: sm.sm_local_gemm_reduce_ws(pm, bxm, ba, bom, wsm, sm.SM_ALLREDUCE, 0, 1, stream),
+                         clock_warm=True)
+    mstep_cold = cold(lambda i: (lambda q=(ba if i == 0 else sm.buf(A.clone())):
+                                 sm.sm_local_gemm_reduce_ws(pm, bxm, q, bom, wsm, sm.SM_ALLREDUCE, 0, 1, stream)),
+                      work_ms)
+    medium_step = rate("hbm", work_ms, mstep, mstep_cold)
+    medium_step["workload"] = (f"X[{Mm},{J}] . A[{J},{K}], J split over {{T:{pm.n_partials}}}, all-reduce "
+                               f"(products into the workspace, then the rank-ordered sum)")
+    medium_step["partials_bytes_not_counted"] = 2 * 4.0 * pm.n_units * Mm * K
+    if with_oracle:
+        oracle_sample(medium_step, lambda: ref.allreduce(qm, ref.partials(qm, Xm_cpu, Ac)), work_ms,
+                      f"the whole step: {qm.n_units} partials of [{Mm},{qm.a_local[1]}]x[{qm.a_local[1]},{K}] "
+                      f"and their rank-ordered sum")
     return {"workload": f"{w.name}: X[{B_},{J}] . A[{J},{K}], J split over {{T:{p.n_partials}}}, all-reduce",
             "fused_gemm_reduce": {**entry, "partials_bytes_not_counted": extra},
             "split_j_gemm_then_reduce_ms": round(g + r, 4),
             "split_j_gemm_ms": round(g, 4), "reduce_ms": round(r, 4),
-            "medium_batch_local_gemm": medium}
+            "medium_batch_local_gemm": medium,
+            "medium_batch_gemm_reduce": medium_step}
 
 
 def source_digest(paths) -> str:

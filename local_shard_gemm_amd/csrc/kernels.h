@@ -105,20 +105,4 @@ constexpr int kTileM = 256, kTileN = 256, kTileK = 64;
 constexpr int kSkinnyMaxM = 64;
 constexpr int kSkinnyCols = 256;
 
-// Workspace of sm_local_gemm_reduce_ws. Skinny products (fused split-J
-// reduction): arrival counters (one 32-bit word per group and column block,
-// rounded up to 256 bytes), then the groups' N partials, each [M, ldp]
-// float32. Products whose one-launch grid would have fewer tiles than the
-// GPU has CUs (two_pass): the N partials only, written by the tile kernel
-// and summed in rank order by the row kernel.
-struct ReduceWorkspace {
-  int64_t counter_bytes, part_bytes, ldp;
-  int32_t n_colblk;
-  int32_t two_pass;
-};
-// Tiles below which a one-launch fused product over the whole J leaves CUs
-// idle (the MI355X has 256).
-constexpr int64_t kFewTiles = 256;
-
-
 }  // namespace shardmm
