@@ -357,6 +357,13 @@ struct Tile {
   static constexpr int NDMA = NA + 4;           // DMA items per wave and stage
   static constexpr int NMF = 8 * MB;            // MFMAs per wave and stage
   static constexpr int NRD = MB + 16;           // fragment reads per wave and stage
+  // Cache policy of the B loads: the 128-row tile serves local products of
+  // at most 128 rows, one row tile per unit, so every B element is read
+  // once per unit and streams past the caches (non-temporal: a 128-row batch
+  // on [3584, 8192] x 8 B blocks ran 88 -> 86 us, 65 rows 86 -> 80 us, bit
+  // for bit the same). The 256-row tile's B panels are re-read by the unit's
+  // other row tiles and keep the default policy.
+  static constexpr int B_AUX = MB == 4 ? 2 : 0;
   // Fragment read issued after MFMA idx of a stage (-1: none). Item i < MB:
   // A fragment i; item MB + 2 ni + t: read t of B fragment ni. Every read
   // overwrites registers last used at least 15 MFMAs earlier (a fragment of
@@ -652,7 +659,8 @@ __device__ __forceinline__ void run_tile_lds(const GemmLaunch& L, const uint16_t
       const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
           (void*)(b_tile + kt_load * b_step), (short)0, 0x7fffffff, 0x00020000);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          r, (lds_void*)(smem + sb + T::A_ST + (4 * wave + item - T::NA) * 1024), 16, vb[item - T::NA], 0, 0, 0);
+          r, (lds_void*)(smem + sb + T::A_ST + (4 * wave + item - T::NA) * 1024), 16, vb[item - T::NA], 0, 0,
+          T::B_AUX);
     }
   };
 
