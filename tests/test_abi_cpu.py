@@ -347,6 +347,15 @@ def test_skinny_fused_reduce_workspace_and_validation():
     # check, which refuses the fake pointers (or finds no device at all)
     assert _err(sm.sm_local_gemm_reduce_ws, sk, X, A, out, ws) in (sm.SM_ERR_ARG, sm.SM_ERR_HIP)
     assert "A: " in sm.sm_last_error()
+    # few-tile taller products: a misaligned workspace is refused; a smaller
+    # one, or none, is accepted (the single launch) and the call reaches the
+    # device-memory check
+    fA, fB, fo = _fb(128, dt=BF), _fb(64, dt=BF), _fb(64)
+    fneed = sm.sm_gemm_reduce_workspace(few)
+    assert _err(sm.sm_local_gemm_reduce_ws, few, fA, fB, fo, (FAKE + 16, fneed)) == sm.SM_ERR_ALIGN
+    for w in ((FAKE, fneed), (FAKE, fneed - 4), None):
+        assert _err(sm.sm_local_gemm_reduce_ws, few, fA, fB, fo, w) in (sm.SM_ERR_ARG, sm.SM_ERR_HIP)
+        assert "A: " in sm.sm_last_error()
 
 
 def test_reduce_and_gather_validation():

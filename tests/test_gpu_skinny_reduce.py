@@ -255,3 +255,48 @@ def test_full_medium_batch_fused_reduce():
         fr = ref.freivalds(X, (0, 0, 128, 28672), A, (0, 0, 28672, 8192), g, trials=1, ints=False)
         say("medium fused", name, "rows rel err", err, "freivalds", fr)
         assert err <= REL_TOL and fr <= FREIVALDS_FLOAT_TOL
+
+
+@pytest.mark.parametrize("mode", [sm.SM_ALLREDUCE, sm.SM_REDUCESCATTER], ids=["AR", "RS"])
+def test_few_tile_products_stacked_subsets_and_fallback(mode):
+    """The few-tile two-launch path with stacked outputs and a subset of the
+    groups (group 1 of 2, then both), bit for bit the oracle's rank-order
+    sums on integers; a workspace one word short of the partials falls back
+    to the single launch, bit for bit sm_local_gemm_reduce."""
+    mesh, sa, sb, I, J, K = {"X": 2, "T": 4}, "P('X', 'T')", "P('T', None)", 2 * 96, 4 * 100, 296
+    say("case: few-tile stacked/subset", mode)
+    A = wl.random_ints((I, J), 831)
+    B = wl.random_ints((J, K), 832)
+    p = sm.sm_plan(mesh, sa, sb, I, J, K)
+    q = planner.plan(mesh, sa, sb, I, J, K)
+    m, n = q.c_local
+    N, G = q.n_partials, q.n_groups
+    Ad, Bd = to_dev(A), to_dev(B)
+    parts = [ref.unit_partial(q, A, B, u) for u in range(q.n_units)]
+    sums = ref.allreduce(q, parts)
+    rs = mode == sm.SM_REDUCESCATTER
+    orows = m // N if rs else m
+    nblk = N if rs else 1
+    for g0, gc in ((1, 1), (0, 2)):
+        nbytes = sm.sm_gemm_reduce_workspace(p, gc)
+        assert nbytes == gc * N * m * 296 * 4
+        ws = torch.full((nbytes // 4,), float("nan"), device=DEV)
+        fs, st = guarded((gc * nblk, orows, n), torch.float32)
+        sm.sm_local_gemm_reduce_ws(p, sm.buf(Ad), sm.buf(Bd), sm.buf(st, block_stride=orows * n), ws, mode, g0, gc)
+        torch.cuda.synchronize()
+        assert guard_intact(fs, st.numel())
+        got = st.cpu().numpy()
+        for i, g in enumerate(range(g0, g0 + gc)):
+            for y in range(nblk):
+                want = sums[g][y * orows:(y + 1) * orows]
+                assert f32_bits_equal(got[i * nblk + y], want), (g, y)
+    # fallback: a workspace too small for the partials
+    nbytes = sm.sm_gemm_reduce_workspace(p)
+    small = torch.empty(nbytes // 4 - 1, device=DEV)
+    a = torch.full((I, K), float("nan"), device=DEV)
+    sm.sm_local_gemm_reduce_ws(p, sm.buf(Ad), sm.buf(Bd), sm.buf(a), small, mode)
+    b = torch.full((I, K), float("nan"), device=DEV)
+    sm.sm_local_gemm_reduce(p, sm.buf(Ad), sm.buf(Bd), sm.buf(b), mode)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+    assert f32_bits_equal(a.cpu().numpy(), ref.gather(q, sums))
