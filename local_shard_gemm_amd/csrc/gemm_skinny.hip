@@ -270,10 +270,10 @@ __global__ __launch_bounds__(NT) void gemm_skinny_kernel(const GemmLaunch L, con
   }
 
   if constexpr (FUSED) {
-    // Arrival: every thread's partial stores are ordered before the
-    // workgroup barrier (workgroup-scope release), and one thread counts the
-    // workgroup in with a vector atomic that releases at device scope, so
-    // the whole workgroup's stores happen before the count. The last of the
+    // Arrival: every wave's partial stores complete before the workgroup
+    // barrier, and one thread counts the workgroup in with a vector atomic
+    // that releases at device scope, so the whole workgroup's stores are
+    // visible before the count. The last of the
     // N arrivals acquires (every thread) and finishes the block. No
     // workgroup ever waits for another. One device-scope release (an L2
     // write-back) per workgroup, not one per wave: on the [16, 28672] x
@@ -282,6 +282,13 @@ __global__ __launch_bounds__(NT) void gemm_skinny_kernel(const GemmLaunch L, con
     __shared__ int s_last;
     const int group = blockIdx.y / R.n_partials;
     uint32_t* counter = R.counters + group * R.n_colblk + blockIdx.x;
+    // Each wave waits until its own device-scope partial stores have
+    // completed. The device-scope release below waits only for the
+    // releasing wave's memory operations, and a CU keeps a separate request
+    // queue per L2 channel, so another wave's stores still in flight could
+    // otherwise reach their channels after the count. (The "memory" clobber
+    // keeps the compiler from moving the stores below the wait.)
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
     __syncthreads();
     if (tid == 0) {
