@@ -478,7 +478,7 @@ def main() -> int:
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: every logical rank's shards are resident on a single "
-              "MI355X; runs on more than one GPU are not part of this build.", file=sys.stderr)
+              "MI355X; the library has no multi-GPU path to measure.", file=sys.stderr)
         return 2
     if args.copy_calibration:
         copy_calibration(args.copy_calibration, 5)
