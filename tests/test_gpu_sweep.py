@@ -14,6 +14,8 @@ A.B (fp64 from the stored inputs; integers keep every fp32 sum exact):
   sm_reduce_partials (all-reduce and, when the rows split, reduce-scatter),
   sm_local_gemm_reduce_ws, and the single-launch sm_local_gemm_reduce for
   products of more than 64 rows;
+- reshards (a separate sweep): random source and target specs on random
+  meshes, bf16 and float32, against the oracle's blocks;
 - cases 2 and 4: the operand the plan names gathered with
   sm_gather_shards and the re-plan from sm_plan_gathered, repeated until
   the plan is case 1 or 3 (a case-4 plan can leave a case-2 one), then as
@@ -187,3 +189,61 @@ def test_random_plans_bitexact(seed):
         q = planner.gathered(q)
         assert p.kase == q.case
     _check_products(p, q, A, B, Ad, Bd, dense)
+
+
+def _random_reshard(seed):
+    rng = np.random.default_rng(8000 + seed)
+    while True:
+        n_axes = int(rng.integers(1, 4))
+        sizes = [int(rng.choice([1, 2, 2, 3, 4])) for _ in range(n_axes)]
+        if int(np.prod(sizes)) <= 12:
+            break
+    mesh = {AXES[a]: sizes[a] for a in range(n_axes)}
+
+    def assign():
+        dims = ([], [])
+        for a in rng.permutation(n_axes):
+            slot = int(rng.integers(0, 3))
+            if slot < 2:
+                dims[slot].append(AXES[a])
+        return dims
+
+    frm, to = assign(), assign()
+    prod = lambda d: int(np.prod([mesh[x] for x in d])) if d else 1  # noqa: E731
+    rows = int(np.lcm(prod(frm[0]), prod(to[0]))) * int(rng.integers(1, 41))
+    cols = 8 * int(np.lcm(prod(frm[1]), prod(to[1]))) * int(rng.integers(1, 17))
+    dtype = sm.SM_BF16 if rng.random() < 0.5 else sm.SM_F32
+    return mesh, _spec_text(frm), _spec_text(to), rows, cols, dtype
+
+
+@pytest.mark.parametrize("seed", range(48))
+def test_random_reshards_bitexact(seed):
+    """sm_reshard between random specs on random meshes (learntpu.dev ch05,
+    "The four collectives and their cost": all-to-all, all-gather, slicing),
+    stacked blocks in and out, bit for bit the oracle's blocks; the global
+    source layout gives the same blocks."""
+    mesh, frm, to, R, Cc, dtype = _random_reshard(seed)
+    say("case: reshard sweep", seed, mesh, frm, to, R, Cc, dtype)
+    tdt = torch.bfloat16 if dtype == sm.SM_BF16 else torch.float32
+    X = wl.random_normal((R, Cc), 8500 + seed)
+    if dtype == sm.SM_F32:
+        X = X.float()
+    stored = ref.stored(X)[0]
+    src_blocks = ref.shard(stored, mesh, frm)
+    want = ref.reshard(src_blocks, mesh, frm, to, R, Cc)
+    src_np = np.stack([src_blocks[b] for b in sorted(src_blocks)])
+    src = torch.from_numpy(src_np)
+    src = (src.view(torch.bfloat16) if dtype == sm.SM_BF16 else src).to(DEV)
+    nb = len(want)
+    br, bc = next(iter(want.values())).shape
+    full = torch.full((nb * br * bc + 256,), 7, dtype=tdt, device=DEV)
+    dst = full[:nb * br * bc].view(nb, br, bc)
+    sm.sm_reshard(mesh, frm, to, R, Cc, dtype, sm.buf(src), sm.buf(dst))
+    dst2 = torch.empty_like(dst)
+    sm.sm_reshard(mesh, frm, to, R, Cc, dtype, sm.buf(X.to(DEV), block_stride=0), sm.buf(dst2))
+    torch.cuda.synchronize()
+    got = ref.stored(dst.cpu())[0]
+    for b in range(nb):
+        np.testing.assert_array_equal(got[b], want[b])
+    assert bool((full[nb * br * bc:] == 7).all())
+    assert torch.equal(dst2, dst)
