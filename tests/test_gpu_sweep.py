@@ -16,6 +16,8 @@ A.B (fp64 from the stored inputs; integers keep every fp32 sum exact):
   products of more than 64 rows;
 - reshards (a separate sweep): random source and target specs on random
   meshes, bf16 and float32, against the oracle's blocks;
+- the sequence-parallel tail (a third sweep) on random case-3 plans with
+  whole output rows, within 1e-5 of the oracle's tail;
 - cases 2 and 4: the operand the plan names gathered with
   sm_gather_shards and the re-plan from sm_plan_gathered, repeated until
   the plan is case 1 or 3 (a case-4 plan can leave a case-2 one), then as
@@ -247,3 +249,61 @@ def test_random_reshards_bitexact(seed):
         np.testing.assert_array_equal(got[b], want[b])
     assert bool((full[nb * br * bc:] == 7).all())
     assert torch.equal(dst2, dst)
+
+
+LN_TOL_INT = 1e-5  # exact pre-norm sums; float32 mean, variance and scaling
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_random_sp_tails(seed):
+    """sm_reduce_scatter_layernorm (ana-alekseeva.com "Sequence parallelism":
+    reduce-scatter, per-token layer norm on the owned rows, all-gather) on
+    random case-3 plans with whole output rows, with and without gamma/beta,
+    against the oracle's tail on the oracle's partials (integer inputs: the
+    sums are exact, the norm is compared within 1e-5); the stacked output
+    gathered equals the global one bit for bit."""
+    rng = np.random.default_rng(8800 + seed)
+    while True:
+        n_axes = int(rng.integers(1, 4))
+        sizes = [int(rng.choice([1, 2, 2, 3, 4])) for _ in range(n_axes)]
+        if int(np.prod(sizes)) <= 8:
+            break
+    mesh = {AXES[a]: sizes[a] for a in range(n_axes)}
+    i_ax, j_ax = [], []
+    for a in rng.permutation(n_axes):
+        (i_ax if rng.random() < 0.4 else j_ax).append(AXES[a])
+    if not j_ax:
+        j_ax, i_ax = i_ax[-1:], i_ax[:-1]
+    prod = lambda d: int(np.prod([mesh[x] for x in d])) if d else 1  # noqa: E731
+    N = prod(j_ax)
+    I = prod(i_ax) * N * int(rng.integers(1, 41))
+    J = N * int(rng.integers(1, 65))
+    K = 4 * int(rng.integers(1, 300))
+    sa, sb = _spec_text((i_ax, j_ax)), _spec_text((j_ax, []))
+    say("case: sp tail sweep", seed, mesh, sa, sb, I, J, K)
+    p = sm.sm_plan(mesh, sa, sb, I, J, K)
+    q = planner.plan(mesh, sa, sb, I, J, K)
+    assert p.kase == q.case == sm.SM_CASE3 and p.c_grid[1] == 1
+    A = wl.random_ints((I, J), 8900 + seed)
+    B = wl.random_ints((J, K), 8950 + seed)
+    Ad, Bd = _place(A), _place(B)
+    m, n = p.c_local
+    P = _stacked(p.n_units, m, n, torch.float32)
+    sm.sm_local_gemm(p, sm.buf(Ad), sm.buf(Bd), sm.buf(P))
+    parts = [ref.unit_partial(q, A, B, u) for u in range(q.n_units)]
+    gamma = rng.standard_normal(K).astype(np.float32)
+    beta = rng.standard_normal(K).astype(np.float32)
+    for g_, b_ in ((None, None), (gamma, beta)):
+        gd = None if g_ is None else torch.from_numpy(g_).to(DEV)
+        bd = None if b_ is None else torch.from_numpy(b_).to(DEV)
+        out = torch.full((I, K), float("nan"), device=DEV)
+        sm.sm_reduce_scatter_layernorm(p, sm.buf(P), sm.buf(out), gd, bd, 1e-5)
+        st = torch.full((p.n_groups * p.n_partials, m // p.n_partials, K), float("nan"), device=DEV)
+        sm.sm_reduce_scatter_layernorm(p, sm.buf(P), sm.buf(st), gd, bd, 1e-5)
+        ag = torch.full((I, K), float("nan"), device=DEV)
+        sm.sm_gather_shards(p, sm.SM_WHAT_C_SCATTERED, sm.buf(st), sm.buf(ag))
+        torch.cuda.synchronize()
+        want = ref.sp_tail(q, parts, g_, b_, 1e-5)
+        err = ref.rel_frobenius(out.cpu().numpy(), want)
+        assert err <= LN_TOL_INT, err
+        assert torch.equal(ag, out)
