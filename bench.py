@@ -595,6 +595,7 @@ def main() -> int:
     gemm_avg = back_to_back(gemm, args.steps)
     red_avg = back_to_back(reduce, args.steps) if p.kase == sm.SM_CASE3 else 0.0
     gemm_single = single_launches(gemm, args.steps)
+    red_single = single_launches(reduce, args.steps) if p.kase == sm.SM_CASE3 else None
     plan_us = plan_time_us(ctx)
 
     m, n = p.c_local[0], p.c_local[1]
@@ -697,6 +698,8 @@ def main() -> int:
                  "tflops": round(gemm_tflops, 1), "frac_of_peak": round(gemm_tflops / PEAK_BF16_TFLOPS, 4),
                  "bytes": gemm_bytes, "gbps": round(gemm_gbps, 1)},
         "reduce": {"avg_ms": round(red_avg, 4), "bytes": red_bytes,
+                   **({"single_launch_median_ms": round(red_single[0], 4),
+                       "single_launch_min_ms": round(red_single[1], 4)} if red_single else {}),
                    "cold_avg_ms": round(red_cold, 4) if red_cold else None,
                    "gbps": round(red_gbps, 1), "frac_of_peak": round(red_gbps / PEAK_HBM_GBPS, 4),
                    "warm_gbps": round(red_gbps_warm, 1)},
