@@ -97,6 +97,9 @@ REF_MUTANTS = {
         ("bi, bk = divmod(g, plan.c_grid[1])", "bk, bi = divmod(g, plan.c_grid[0])"),
     "scattered gather: every row block at its group's start":
         ("r0, rows = plan.rs_rows(g, y)", "r0, rows = plan.rs_rows(g, 0)"),
+    "per-rank all-reduce output indexed by the rank's partial, not its group":
+        ("return {r: sums[plan.rank_unit(r) // plan.n_partials] for r in range(plan.n_ranks)}",
+         "return {r: sums[plan.rank_unit(r) % plan.n_partials] for r in range(plan.n_ranks)}"),
     "gather of partials accepted":
         ("if plan.case == 3 and plan.n_partials > 1:", "if False:"),
     "layer norm: unbiased variance":

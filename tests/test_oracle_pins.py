@@ -202,6 +202,25 @@ def test_generalised_case3_groups():
         np.testing.assert_array_equal(sums[g], D[g * 8:(g + 1) * 8])
 
 
+def test_rank_outputs_after_allreduce():
+    """semiaifoundry.com "Sharded matrix multiplication and result
+    ownership" (The mechanism: after the all-reduce every rank holds the
+    completed values of its block): on {X:2, Y:2} with A[I_X, J_Y], rank
+    (x, y) holds rows x*m.. of the dense product (numpy), the same block for
+    both y, and ranks of different x hold different row blocks."""
+    A = _ints((16, 24), 55)
+    B = _ints((24, 12), 56)
+    D = A @ B
+    p = planner.plan({"X": 2, "Y": 2}, "P('X', 'Y')", "P('Y', None)", 16, 24, 12)
+    held = ref.rank_outputs_allreduce(p, ref.partials(p, A, B))
+    assert sorted(held) == [0, 1, 2, 3]
+    for r, blk in held.items():
+        x = r // 2  # row-major rank numbering over (X, Y)
+        np.testing.assert_array_equal(blk, D[x * 8:(x + 1) * 8])
+    np.testing.assert_array_equal(held[0], held[1])
+    assert not np.array_equal(held[0], held[2])
+
+
 def test_integer_exactness_bound():
     """Closed form (IEEE binary32 has a 24-bit significand): with entries in
     [-4, 4] every partial sum is an integer of magnitude <= 16 J, exact in
