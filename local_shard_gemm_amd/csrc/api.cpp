@@ -439,9 +439,11 @@ ReduceWorkspace reduce_workspace(const sm_plan_t& p, int64_t groups) {
 // sm_local_gemm_reduce (no scratch), sm_local_gemm_reduce_ws (the caller's
 // workspace) and the no-allocation entry point (the library's static
 // scratch). Products of more than 64 rows: one tile-kernel launch per batch
-// of groups, K = the group's whole J, no scratch. Skinny products: the
-// split-J kernel with the fused reduction, whose counters and partials live
-// in the scratch `sc` describes.
+// of groups, K = the group's whole J, no scratch; or, when that launch would
+// have few tiles and the scratch holds the partials, the units' products into
+// the scratch (one tile-kernel launch) and their rank-ordered sum (one row
+// launch). Skinny products: the split-J kernel with the fused reduction,
+// whose counters and partials live in the scratch `sc` describes.
 int32_t gemm_reduce_impl(const sm_plan_t* plan, const sm_buf* A, const sm_buf* B, const sm_buf* out, int32_t mode,
                          int32_t group_begin, int32_t group_count, const ReduceScratch& sc, void* stream,
                          const char* where) {

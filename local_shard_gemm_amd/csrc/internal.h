@@ -74,10 +74,11 @@ struct ReduceWorkspace {
 constexpr int64_t kFewTiles = 256;
 // Workspace layout of a fused reduction over `groups` groups.
 ReduceWorkspace reduce_workspace(const sm_plan_t& p, int64_t groups);
-// Where a fused skinny reduction keeps its counters and partials.
+// Where a fused reduction keeps its counters and partials (skinny products),
+// or its partials (few-tile taller products).
 struct ReduceScratch {
   enum Kind : int32_t {
-    kNone = 0,      // none (sm_local_gemm_reduce): skinny products are refused
+    kNone = 0,      // none (sm_local_gemm_reduce): skinny products are refused, taller ones run as one launch
     kCaller = 1,    // the caller's workspace `ws`, split as documented for sm_local_gemm_reduce_ws
     kFixed = 2,     // fixed regions (the static scratch): counters, then partials, each with a capacity
     kValidate = 3,  // run every host check, launch nothing
