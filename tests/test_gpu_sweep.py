@@ -18,6 +18,8 @@ A.B (fp64 from the stored inputs; integers keep every fp32 sum exact):
   meshes, bf16 and float32, against the oracle's blocks;
 - the sequence-parallel tail (a third sweep) on random case-3 plans with
   whole output rows, within 1e-5 of the oracle's tail;
+- the GeLU -> bfloat16 epilogue (a fourth sweep) on random case-1 plans,
+  within the derived bound of the oracle's round_bf16(gelu(.));
 - cases 2 and 4: the operand the plan names gathered with
   sm_gather_shards and the re-plan from sm_plan_gathered, repeated until
   the plan is case 1 or 3 (a case-4 plan can leave a case-2 one), then as
@@ -307,3 +309,52 @@ def test_random_sp_tails(seed):
         err = ref.rel_frobenius(out.cpu().numpy(), want)
         assert err <= LN_TOL_INT, err
         assert torch.equal(ag, out)
+
+
+@pytest.mark.parametrize("seed", range(32))
+def test_random_gelu_epilogues(seed):
+    """The GeLU(tanh) -> bfloat16 epilogue (ana-alekseeva.com "MLP block":
+    GeLU applies to each column block of the first layer) on random case-1
+    plans (random meshes, A sharded on I or not, B on K, ragged sizes, row
+    padding holding NaN): every unit's stacked bfloat16 block within the
+    derived bound of the oracle's round_bf16(gelu(A_u B_u)), and fewer than
+    1 % of its elements differ at all."""
+    from hip_cases import gelu_h_within_bound
+
+    rng = np.random.default_rng(9300 + seed)
+    while True:
+        n_axes = int(rng.integers(1, 4))
+        sizes = [int(rng.choice([1, 2, 2, 3, 4])) for _ in range(n_axes)]
+        if int(np.prod(sizes)) <= 8:
+            break
+    mesh = {AXES[a]: sizes[a] for a in range(n_axes)}
+    i_ax, k_ax = [], []
+    for a in rng.permutation(n_axes):
+        slot = int(rng.integers(0, 3))
+        if slot == 0:
+            i_ax.append(AXES[a])
+        elif slot == 1:
+            k_ax.append(AXES[a])
+    prod = lambda d: int(np.prod([mesh[x] for x in d])) if d else 1  # noqa: E731
+    I = prod(i_ax) * int(rng.integers(1, 161))
+    J = int(rng.integers(1, 200))
+    K = prod(k_ax) * int(rng.integers(1, 161))
+    sa, sb = _spec_text((i_ax, [])), _spec_text(([], k_ax))
+    say("case: gelu sweep", seed, mesh, sa, sb, I, J, K)
+    p = sm.sm_plan(mesh, sa, sb, I, J, K, out_dtype=sm.SM_BF16)
+    q = planner.plan(mesh, sa, sb, I, J, K)
+    assert p.kase == q.case == sm.SM_CASE1
+    X = wl.random_normal((I, J), 9400 + seed)
+    W = wl.random_normal((J, K), 9450 + seed, 0.1)
+    m, n = p.c_local
+    H = _stacked(p.n_units, m, n, torch.bfloat16)
+    sm.sm_local_gemm(p, sm.buf(_place(X)), sm.buf(_place(W)), sm.buf(H), sm.SM_EPI_GELU_TANH)
+    torch.cuda.synchronize()
+    Hg = H[:, :, :n].contiguous().cpu().view(torch.int16).numpy().view(np.uint16)
+    absdot = ref.matmul(np.abs(ref.widen(X)), np.abs(ref.widen(W)))
+    for u in range(p.n_units):
+        want = ref.round_bf16(ref.gelu_tanh(ref.unit_partial(q, X, W, u)))
+        r0, c0, _, _ = q.unit_views(u)["C"]
+        ok = gelu_h_within_bound(Hg[u], want, absdot[r0:r0 + m, c0:c0 + n], J)
+        assert ok.all(), (u, int((~ok).sum()))
+        assert (Hg[u] != want).mean() < 0.01, u
