@@ -208,7 +208,9 @@ int32_t sm_rank_info(const sm_plan_t* plan, int32_t rank, sm_rank_info_t* out);
  * when a case-4 fix leaves the other operand sharded on J (call again).
  * The gather itself is sm_gather_shards with
  * SM_WHAT_A / SM_WHAT_B into the global layout, whose views serve any
- * partial gather. Errors: SM_ERR_CASE for case-1/3 plans. */
+ * partial gather. Errors: SM_ERR_CASE for case-1/3 plans;
+ * SM_ERR_J_MISMATCH when, after a case-4 fix, A and B shard J over
+ * different axis lists (a reshard of J is needed first). */
 int32_t sm_plan_gathered(const sm_plan_t* plan, sm_plan_t* out);
 
 /* Local products C_u = A_u . B_u for units [unit_begin, unit_begin+count):
